@@ -1,0 +1,252 @@
+"""Pins for the binary64 oracle, against things other than itself.
+
+Each pin is chosen so that a plausible slip in the oracle (a dropped term, a
+wrong sign, scale or index, a transposed operand, a wrong head grouping, a
+leaking mask) fails at least one of them:
+
+* a library routine: torch's binary64 scaled_dot_product_attention and its
+  autograd (forward O, the natural-log logsumexp for L, dQ/dK/dV);
+* central finite differences of f = sum(O * dO) (gradients);
+* closed forms: zero keys (prefix means, L = log2(i+1), dV closed form), the
+  first causal row, constant values, and a two-token example worked by hand
+  (tests/golden/two_token_worked_example.json);
+* invariants: shift of every key by one vector, grouped heads equal to
+  repeated heads, variable length equal to per-sequence runs, zeros on masked
+  rows and keys, sum_j dK_j = 0 and sum_j dV_j = sum of the admitted dO rows.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from causal_streaming_attention_amd.workloads import SCALE, make_inputs
+
+LN2 = math.log(2.0)
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _t64(x):
+    return torch.from_numpy(np.asarray(x, dtype=np.float64))
+
+
+def torch_reference(Q, K, Vt, dO, causal, seqlens=None, scale=SCALE):
+    """Library-routine reference: SDPA in float64 on the CPU with autograd.
+    K/V heads are repeated contiguously for grouped heads; autograd of the
+    repeat sums the gradients over each group.  Variable-length sequences are
+    run one by one on their unpadded prefix."""
+    B, H, T, _ = Q.shape
+    KV = K.shape[1]
+    G = H // KV
+    out = {"O": np.zeros((B, H, T, 64)), "L": np.full((B, H, T), -np.inf),
+           "dQ": np.zeros((B, H, T, 64)), "dK": np.zeros((B, KV, T, 64)), "dVt": np.zeros((B, KV, 64, T))}
+    for b in range(B):
+        n = T if seqlens is None else int(seqlens[b])
+        if n == 0:
+            continue
+        q = _t64(Q[b, :, :n]).requires_grad_()
+        k = _t64(K[b, :, :n]).requires_grad_()
+        v = _t64(np.swapaxes(Vt[b, :, :, :n], -1, -2)).requires_grad_()
+        kk = k.repeat_interleave(G, dim=0)
+        vv = v.repeat_interleave(G, dim=0)
+        o = torch.nn.functional.scaled_dot_product_attention(q[None], kk[None], vv[None], is_causal=causal,
+                                                             scale=scale)[0]
+        (o * _t64(dO[b, :, :n])).sum().backward()
+        s = (q @ kk.transpose(-1, -2)) * scale
+        if causal:
+            s = s.masked_fill(torch.triu(torch.ones(n, n, dtype=torch.bool), 1), -math.inf)
+        out["O"][b, :, :n] = o.detach().numpy()
+        out["L"][b, :, :n] = (torch.logsumexp(s, dim=-1) / LN2).detach().numpy()
+        out["dQ"][b, :, :n] = q.grad.numpy()
+        out["dK"][b, :, :n] = k.grad.numpy()
+        out["dVt"][b, :, :, :n] = np.swapaxes(v.grad.numpy(), -1, -2)
+    return out
+
+
+CASES = [
+    # B, T, H, KV, causal, varlen
+    (1, 96, 2, 2, True, False),
+    (2, 130, 4, 2, True, False),
+    (1, 80, 3, 1, False, False),
+    (3, 100, 4, 2, False, True),
+    (3, 70, 2, 1, True, True),
+]
+
+
+@pytest.mark.parametrize("B,T,H,KV,causal,varlen", CASES)
+def test_oracle_matches_torch_sdpa_and_autograd(B, T, H, KV, causal, varlen):
+    x = make_inputs(B, T, H, KV, seed=11 + T, varlen=varlen)
+    if varlen:
+        x["seqlens"][0] = 0            # an empty sequence: every row fully masked
+    r = oracle.backward(x["Q"], x["K"], x["Vt"], x["dO"], s=SCALE, causal=causal, seqlens=x["seqlens"])
+    ref = torch_reference(x["Q"], x["K"], x["Vt"], x["dO"], causal, x["seqlens"])
+    np.testing.assert_allclose(r["O"], ref["O"], rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(np.isneginf(r["L"]), np.isneginf(ref["L"]))
+    fin = np.isfinite(ref["L"])
+    np.testing.assert_allclose(r["L"][fin], ref["L"][fin], rtol=0, atol=1e-11)
+    for k in ("dQ", "dK", "dVt"):
+        np.testing.assert_allclose(r[k], ref[k], rtol=0, atol=1e-11, err_msg=k)
+
+
+def _f_value(Q, K, Vt, dO, causal, seqlens):
+    O, _ = oracle.forward(Q, K, Vt, s=SCALE, causal=causal, seqlens=seqlens)
+    return float(np.sum(O * dO))
+
+
+@pytest.mark.parametrize("causal,seqlens", [(True, None), (False, [9, 4]), (True, [12, 7])])
+def test_oracle_gradients_match_finite_differences(causal, seqlens):
+    rng = np.random.default_rng(5)
+    B = 1 if seqlens is None else len(seqlens)
+    T, H, KV = 12, 2, 1
+    Q = rng.standard_normal((B, H, T, 64))
+    K = rng.standard_normal((B, KV, T, 64))
+    Vt = rng.standard_normal((B, KV, 64, T))
+    dO = rng.standard_normal((B, H, T, 64))
+    sl = None if seqlens is None else np.array(seqlens, dtype=np.int32)
+    g = oracle.backward(Q, K, Vt, dO, s=SCALE, causal=causal, seqlens=sl)
+    h = 1e-5
+    for name, arr, grad in (("Q", Q, g["dQ"]), ("K", K, g["dK"]), ("Vt", Vt, g["dVt"])):
+        idx = [tuple(rng.integers(0, n) for n in arr.shape) for _ in range(24)]
+        for ix in idx:
+            orig = arr[ix]
+            arr[ix] = orig + h
+            fp = _f_value(Q, K, Vt, dO, causal, sl)
+            arr[ix] = orig - h
+            fm = _f_value(Q, K, Vt, dO, causal, sl)
+            arr[ix] = orig
+            fd = (fp - fm) / (2 * h)
+            assert abs(fd - grad[ix]) <= 1e-7 * max(1.0, abs(fd)), (name, ix, fd, grad[ix])
+
+
+def test_oracle_two_token_worked_example():
+    with open(os.path.join(HERE, "golden", "two_token_worked_example.json")) as f:
+        g = json.load(f)
+    T = g["T"]
+    Q = np.zeros((1, 1, T, 64)); K = np.zeros((1, 1, T, 64)); V = np.zeros((1, 1, T, 64)); dO = np.zeros((1, 1, T, 64))
+    for name, arr in (("Q", Q), ("K", K), ("V", V), ("dO", dO)):
+        for i, d, v in g["inputs_nonzero"][name]:
+            arr[0, 0, i, d] = v
+    Vt = np.swapaxes(V, -1, -2).copy()
+    r = oracle.backward(Q, K, Vt, dO, s=g["scale"], causal=g["causal"])
+    exp = g["expected_nonzero"]
+    for name, got in (("O", r["O"]), ("dQ", r["dQ"]), ("dK", r["dK"]), ("dV", np.swapaxes(r["dVt"], -1, -2))):
+        want = np.zeros((T, 64))
+        for i, d, v in exp[name]:
+            want[i, d] = v
+        np.testing.assert_allclose(got[0, 0], want, rtol=0, atol=1e-15, err_msg=name)
+    np.testing.assert_allclose(r["L"][0, 0], exp["L"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(r["D"][0, 0], exp["D"], rtol=0, atol=1e-15)
+
+
+def test_oracle_closed_forms_zero_keys():
+    """K = 0: every admitted key scores 0, so P_ij = 1/(i+1) over j <= i."""
+    x = make_inputs(1, 40, 2, 1, seed=3)
+    K = np.zeros_like(x["K"])
+    r = oracle.backward(x["Q"], K, x["Vt"], x["dO"], s=SCALE, causal=True)
+    V = np.swapaxes(x["Vt"].astype(np.float64), -1, -2)[0, 0]        # [T, 64]
+    counts = np.arange(1, 41, dtype=np.float64)
+    prefix_mean = np.cumsum(V, axis=0) / counts[:, None]
+    for h in range(2):
+        np.testing.assert_allclose(r["O"][0, h], prefix_mean, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(r["L"][0, h], np.log2(counts), rtol=0, atol=1e-13)
+    # dV_j = sum over heads and i >= j of dO_i / (i + 1)
+    dO = x["dO"].astype(np.float64)[0]                                   # [H, T, 64]
+    w = dO / counts[None, :, None]
+    suffix = np.cumsum(w[:, ::-1], axis=1)[:, ::-1].sum(axis=0)          # [T, 64]
+    np.testing.assert_allclose(np.swapaxes(r["dVt"][0, 0], 0, 1), suffix, rtol=0, atol=1e-12)
+    assert np.all(r["dQ"] == 0.0)                                        # dQ = s dS K = 0
+
+
+def test_oracle_closed_forms_first_row_and_constant_values():
+    x = make_inputs(1, 64, 1, 1, seed=4)
+    r = oracle.backward(x["Q"], x["K"], x["Vt"], x["dO"], s=SCALE, causal=True)
+    q0 = x["Q"][0, 0, 0].astype(np.float64)
+    k0 = x["K"][0, 0, 0].astype(np.float64)
+    np.testing.assert_allclose(r["O"][0, 0, 0], x["Vt"][0, 0, :, 0].astype(np.float64), rtol=0, atol=0)
+    np.testing.assert_allclose(r["L"][0, 0, 0], float(q0 @ k0) * SCALE / LN2, rtol=1e-14, atol=1e-14)
+    u = np.linspace(-2, 2, 64)
+    Vt = np.broadcast_to(u[None, None, :, None], (1, 1, 64, 64)).copy()
+    O, _ = oracle.forward(x["Q"], x["K"], Vt, s=SCALE, causal=False)
+    np.testing.assert_allclose(O[0, 0], np.broadcast_to(u, (64, 64)), rtol=0, atol=1e-14)
+
+
+def test_oracle_key_shift_invariance():
+    """Adding one vector u to every key adds s/ln2 q_i.u to each row's scores:
+    P and O are unchanged and L_i grows by exactly that amount."""
+    x = make_inputs(1, 50, 2, 1, seed=6)
+    Q = x["Q"].astype(np.float64)
+    u = np.random.default_rng(1).standard_normal(64)
+    K2 = x["K"].astype(np.float64) + u
+    O1, L1 = oracle.forward(Q, x["K"], x["Vt"], s=SCALE, causal=True)
+    O2, L2 = oracle.forward(Q, K2, x["Vt"], s=SCALE, causal=True)
+    np.testing.assert_allclose(O2, O1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L2 - L1, (Q @ u) * SCALE / LN2, rtol=0, atol=1e-11)
+
+
+def test_oracle_grouped_heads_equal_repeated_heads():
+    x = make_inputs(2, 64, 6, 2, seed=8)
+    G = 3
+    Kr = np.repeat(x["K"], G, axis=1)
+    Vr = np.repeat(x["Vt"], G, axis=1)
+    g = oracle.backward(x["Q"], x["K"], x["Vt"], x["dO"], s=SCALE, causal=True)
+    m = oracle.backward(x["Q"], Kr, Vr, x["dO"], s=SCALE, causal=True)
+    for k in ("O", "L", "D", "dQ"):
+        np.testing.assert_allclose(g[k], m[k], rtol=0, atol=1e-13, err_msg=k)
+    np.testing.assert_allclose(g["dK"], m["dK"].reshape(2, 2, G, 64, 64).sum(axis=2), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(g["dVt"], m["dVt"].reshape(2, 2, G, 64, 64).sum(axis=2), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_oracle_varlen_equals_per_sequence_and_masks_padding(causal):
+    lens = [37, 0, 64, 1]
+    x = make_inputs(4, 64, 2, 2, seed=9, seqlens=lens)
+    r = oracle.backward(x["Q"], x["K"], x["Vt"], x["dO"], s=SCALE, causal=causal, seqlens=x["seqlens"])
+    for b, n in enumerate(lens):
+        if n > 0:
+            one = oracle.backward(x["Q"][b:b + 1, :, :n], x["K"][b:b + 1, :, :n], x["Vt"][b:b + 1, :, :, :n],
+                                  x["dO"][b:b + 1, :, :n], s=SCALE, causal=causal)
+            for k in ("O", "L", "D", "dQ", "dK"):
+                np.testing.assert_array_equal(r[k][b:b + 1, :, :n], one[k], err_msg=k)
+            np.testing.assert_array_equal(r["dVt"][b:b + 1, :, :, :n], one["dVt"])
+        assert np.all(r["O"][b, :, n:] == 0) and np.all(np.isneginf(r["L"][b, :, n:]))
+        assert np.all(r["D"][b, :, n:] == 0) and np.all(r["dQ"][b, :, n:] == 0)
+        assert np.all(r["dK"][b, :, n:] == 0) and np.all(r["dVt"][b, :, :, n:] == 0)
+
+
+def test_oracle_gradient_sums():
+    """sum_j dS_ij = 0 for every row gives sum_j dK_j = 0; rows of P sum to 1
+    give sum_j dV_j = sum over the group's heads of the admitted dO rows."""
+    lens = [50, 64]
+    x = make_inputs(2, 64, 4, 2, seed=10, seqlens=lens)
+    r = oracle.backward(x["Q"], x["K"], x["Vt"], x["dO"], s=SCALE, causal=True, seqlens=x["seqlens"])
+    dO = x["dO"].astype(np.float64)
+    for b, n in enumerate(lens):
+        for kv in range(2):
+            np.testing.assert_allclose(r["dK"][b, kv].sum(axis=0), 0.0, atol=1e-11)
+            want = dO[b, 2 * kv:2 * kv + 2, :n].sum(axis=(0, 1))
+            np.testing.assert_allclose(r["dVt"][b, kv].sum(axis=1), want, rtol=0, atol=1e-11)
+
+
+def test_oracle_row_and_column_subsets_match_full_sweep():
+    x = make_inputs(2, 64, 4, 2, seed=12, varlen=True)
+    full = oracle.backward(x["Q"], x["K"], x["Vt"], x["dO"], s=SCALE, causal=True, seqlens=x["seqlens"])
+    rows = np.array([0, 5, 63, 64 * 5 + 7, 2 * 4 * 64 - 1])
+    O, L = oracle.forward_rows(x["Q"], x["K"], x["Vt"], s=SCALE, causal=True, seqlens=x["seqlens"], rows=rows)
+    np.testing.assert_array_equal(O, full["O"].reshape(-1, 64)[rows])
+    np.testing.assert_array_equal(L, full["L"].reshape(-1)[rows])
+    cols = np.array([3, 64 + 40, 3 * 64 + 63])
+    dK, dV = oracle.backward_cols(x["Q"], x["K"], x["Vt"], x["dO"], s=SCALE, causal=True,
+                                  seqlens=x["seqlens"], cols=cols)
+    np.testing.assert_array_equal(dK, full["dK"].reshape(-1, 64)[cols])
+    np.testing.assert_array_equal(dV, np.swapaxes(full["dVt"], -1, -2).reshape(-1, 64)[cols])
+
+
+def test_oracle_rejects_bad_ids_and_shapes():
+    x = make_inputs(1, 64, 2, 1, seed=1)
+    with pytest.raises(ValueError):
+        oracle.forward_rows(x["Q"], x["K"], x["Vt"], s=SCALE, causal=True, rows=[128])
+    with pytest.raises(ValueError):
+        oracle.forward(x["Q"], x["K"][:, :, :32], x["Vt"], s=SCALE, causal=True)
