@@ -1,0 +1,88 @@
+// sa_device.h -- gfx950 device helpers shared by the attention kernels.
+//
+// Wave64 MFMA v_mfma_f32_32x32x16_f16 operand geometry (lane l, l32 = l % 32,
+// hi = l / 32):
+//   A (32 x 16):  lane holds A[l32][8 hi + t],        t = 0..7
+//   B (16 x 32):  lane holds B[8 hi + t][l32],        t = 0..7
+//   C (32 x 32):  lane holds C[8 (r/4) + 4 hi + r%4][l32], r = 0..15
+// ds_read_b64_tr_b16 (per 16-lane group): the lane with index
+// 4 * row + chunk (within the group) names 4 consecutive halves at
+// (row, 4 * chunk) of the group's 4 x 16 block; afterwards lane i of the
+// group holds that block's column i, rows 0..3.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+typedef _Float16 half_t;
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __fp16 fp16x4_raw __attribute__((__vector_size__(4 * sizeof(__fp16))));
+
+constexpr int kHeadDim = 64;
+constexpr int kTile = 64;          // keys per tile and rows per dS tile
+constexpr int kLdsRow = 72;        // padded LDS row, in halves (144 bytes)
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ f32x16 mfma32(const half8& a, const half8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+    return z;
+}
+
+// 2^x on the transcendental unit (v_exp_f32): 2^-inf = 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+// log2 x (v_log_f32) and 1/x (v_rcp_f32), about 1 ulp.
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Reductions across the two wave halves (lane l with lane l ^ 32) by one
+// v_permlane32_swap: between them its two results hold both halves' values in
+// every lane, so max and sum are exact and identical in all 64 lanes.
+__device__ __forceinline__ float max_halves(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Round to nearest even binary16.
+__device__ __forceinline__ half_t to_half(float x) { return (half_t)x; }
+
+typedef __attribute__((address_space(3))) fp16x4_raw lds_fp16x4;
+
+// ds_read_b64_tr_b16 at an LDS element pointer (must point into __shared__ memory).
+__device__ __forceinline__ half4 lds_read_tr(const half_t* p) {
+    fp16x4_raw v = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+        (lds_fp16x4*)((__attribute__((address_space(3))) half_t*)(p)));
+    return __builtin_bit_cast(half4, v);
+}
+
+__device__ __forceinline__ half8 cat(const half4& lo, const half4& hi) {
+    half8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+}
+
+// Per-lane element offset, inside a row-major LDS block with row stride
+// kLdsRow, that a transposed read names so that lane l of a wave receives
+// column (col0 + 16 * ((l / 16) % 2) + l % 16) at rows row0(l) + 0..3, where
+// row0 = rowA for lanes 0..31 and rowB for lanes 32..63.
+__device__ __forceinline__ int tr_offset(int lane, int rowA, int rowB, int col0) {
+    int row0 = (lane & 32) ? rowB : rowA;
+    int r = (lane & 15) >> 2, chunk = lane & 3;
+    return (row0 + r) * kLdsRow + col0 + 16 * ((lane >> 4) & 1) + 4 * chunk;
+}
+
+}  // namespace sa

@@ -1,0 +1,40 @@
+// sa_internal.h -- launchers behind the C ABI (no validation here: the
+// entry points in sa_api.cpp check shapes and pointers first).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sa {
+
+struct Shape {
+    int batch, T, heads, kv_heads, causal;
+    const int32_t* seqlens;  // device pointer or nullptr
+    int block_order;
+};
+
+// dS workspace geometry: one fp16 64x64 tile per (batch, query head, query
+// tile qt, key tile kt) that the dQ pass reads.  Causal: kt <= qt, tile index
+// qt (qt + 1) / 2 + kt; otherwise the full square, qt * nt + kt.
+inline size_t ds_tiles_per_head(const Shape& sh) {
+    size_t nt = (size_t)sh.T / 64;
+    return sh.causal ? nt * (nt + 1) / 2 : nt * nt;
+}
+constexpr size_t kDsTileBytes = 64 * 64 * 2;
+
+hipError_t launch_forward(const Shape& sh, const void* Q, const void* K, const void* Vt, void* O, float* L,
+                          float c, hipStream_t stream);
+hipError_t launch_row_terms(const Shape& sh, const void* dO, const void* O, float* D, hipStream_t stream);
+hipError_t launch_key_pass(const Shape& sh, const void* Q, const void* K, const void* Vt, const void* dO,
+                           const float* L, const float* D, void* dS, float c, float s, float* dK, float* dVt,
+                           hipStream_t stream);
+hipError_t launch_dq_pass(const Shape& sh, const void* K, const void* dS, float s, float* dQ,
+                          hipStream_t stream);
+
+// Grid sizes, for the entry points' admission of launch dimensions.
+size_t forward_blocks(const Shape& sh);
+size_t row_terms_blocks(const Shape& sh);
+size_t key_pass_blocks(const Shape& sh);
+size_t dq_pass_blocks(const Shape& sh);
+
+}  // namespace sa

@@ -1,0 +1,176 @@
+/*
+ * sa.h -- causal streaming attention for MI355X (gfx950), head width 64.
+ *
+ * A C ABI over hand-written HIP kernels.  Every entry point takes plain
+ * device pointers, sizes and a HIP stream (as void*, NULL = the default
+ * stream), enqueues its kernels on that stream and returns without
+ * synchronising.  The library never allocates, frees or copies memory of its
+ * own: the caller owns every buffer.  No exception crosses the boundary and
+ * the process is never aborted; every failure is a returned status, checked
+ * before anything is launched (except SA_ERR_DEVICE, reported by the launch).
+ *
+ * The method (StreamingAttentionSM86 page):
+ *   forward  -- banner "Causal attention as a streaming normalised sum":
+ *               softmax(Q K^T scale) V one 64-key tile at a time, with a
+ *               running row maximum m, row sum l and weighted sum O; scores
+ *               in base-2 units t = S c, c the binary32 nearest scale / ln 2;
+ *               P rounded to binary16 before P V; every sum in binary32; the
+ *               output O / l and the base-2 log-sum-exp L = m + log2 l.
+ *   backward -- banners "The backward pass, deterministic and in two
+ *               launches" and "The query pass split in two around the key
+ *               pass": P = 2^(S c - L), dP = dO V^T, D = rowsum(dO * O),
+ *               dS = P (dP - D), dQ = s dS K, dK = s dS^T Q, dV = P^T dO,
+ *               in three launches (row terms, key pass storing dS, dQ pass
+ *               reading it), deterministic and without atomics.
+ *   lengths  -- variable-length gist page (self_attn_fwd): a query or key at
+ *               or past its sequence's length is masked, a row with no
+ *               admitted key has O = 0.
+ *
+ * Grouped query attention: query head h uses K/V head h / (heads/kv_heads)
+ * (contiguous groups).  dK and dV^T are the gradients with respect to the K
+ * and V^T inputs, so they are summed over each group's query heads.
+ *
+ * Layouts (row-major, element offsets; B = batch, H = heads, KV = kv_heads):
+ *   Q   fp16 [B][H][T][64]        K   fp16 [B][KV][T][64]
+ *   Vt  fp16 [B][KV][64][T]       (V transposed, as the pages take it)
+ *   O   fp16 [B][T][H*64]         (token-major, heads merged)
+ *   L   fp32 [B][H][T]            (base-2 log-sum-exp; -inf on masked rows)
+ *   dO  fp16 [B][H][T][64]        D   fp32 [B][H][T]
+ *   dQ  fp32 [B][H][T][64]        dK  fp32 [B][KV][T][64]
+ *   dVt fp32 [B][KV][64][T]
+ *   dS  workspace, sa_backward_workspace_bytes() bytes, contents private.
+ * Every pointer must be non-NULL and 16-byte aligned.
+ *
+ * Rows and keys at or past a sequence's length (padding) never influence a
+ * valid output, whatever the padding holds.  Padded rows get O = 0,
+ * L = -inf, D = 0 and dQ = 0; padded keys get dK = dV = 0.
+ *
+ * Results are bitwise reproducible for equal inputs, shape and block order.
+ * Calls on one stream run in order; calls that share output or workspace
+ * buffers on different streams race.
+ */
+#ifndef SA_H
+#define SA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sa_status {
+    SA_OK = 0,
+    SA_ERR_SHAPE = 1,      /* the shape fails admission (see sa_check_shape) */
+    SA_ERR_NULL = 2,       /* a required pointer is NULL */
+    SA_ERR_ALIGN = 3,      /* a pointer is not 16-byte aligned (seqlens: 4-byte) */
+    SA_ERR_WORKSPACE = 4,  /* dS_bytes < sa_backward_workspace_bytes(shape) */
+    SA_ERR_ARGUMENT = 5,   /* c or s not finite and positive */
+    SA_ERR_DEVICE = 6      /* a HIP launch failed (read, and so cleared, by hipGetLastError) */
+} sa_status;
+
+/*
+ * Problem shape.  Admission (the pages' admission predicate for the grouped
+ * launch, StreamingAttentionSM86 page, forward program, without its 32-bit
+ * offset clause since every offset here is 64-bit):
+ *   batch >= 1;  T >= 64 and T % 64 == 0;  heads >= 1;  kv_heads >= 1;
+ *   heads % kv_heads == 0;  heads <= 65535;  batch * heads <= 2^24;
+ *   T <= 2^20;  causal is 0 or 1;  block_order is 0 or 1.
+ */
+typedef struct sa_shape {
+    int batch;
+    int T;                    /* padded sequence length */
+    int heads;                /* query heads */
+    int kv_heads;             /* key/value heads */
+    int causal;               /* 1: key j admitted for query i only if j <= i */
+    const int32_t* seqlens;   /* device int32[batch] sequence lengths, or NULL
+                                 (every sequence has length T).  Values are
+                                 clamped to [0, T] by the kernels. */
+    int block_order;          /* 0: heavy-first (longest causal blocks first,
+                                 the pages' order 1); 1: natural order.  The
+                                 results are bitwise identical either way. */
+} sa_shape;
+
+/* SA_OK if `shape` passes admission, else SA_ERR_SHAPE (SA_ERR_NULL if NULL).
+ * Host-only: makes no HIP call. */
+sa_status sa_check_shape(const sa_shape* shape);
+
+/*
+ * Forward, batch 1, causal, every sequence of length T (the pages' call).
+ *   Q, K, Vt: inputs (layouts above).  O, L: outputs, fully overwritten.
+ *   c: binary32 nearest scale / ln 2 (e.g. 0x3E38AA3B for scale 1/8).
+ */
+sa_status sa_forward(const void* Q, const void* K, const void* Vt, void* O, float* L, float c,
+                     int T, int heads, int kv_heads, void* stream);
+
+/* Forward for a general shape (batch, causal or not, sequence lengths). */
+sa_status sa_forward_ex(const sa_shape* shape, const void* Q, const void* K, const void* Vt,
+                        void* O, float* L, float c, void* stream);
+
+/*
+ * Bytes of dS workspace sa_backward needs: one fp16 64x64 tile per
+ * (batch, query head, query tile, key tile) the dQ pass reads -- the lower
+ * triangle including the diagonal when causal, the full square otherwise.
+ * Returns 0 if the shape fails admission.
+ */
+size_t sa_backward_workspace_bytes(const sa_shape* shape);
+
+/*
+ * Backward, batch 1, causal, every sequence of length T.
+ *   dO: fp16 output gradient.  O, L: this shape's sa_forward outputs.
+ *   D: fp32 [H][T] row terms, written (an output the caller may ignore).
+ *   dS, dS_bytes: workspace of at least sa_backward_workspace_bytes bytes.
+ *   Q, K, Vt: the forward's inputs.  c: as sa_forward; s: the natural
+ *   score scale (dQ and dK carry it, dV does not).
+ *   dQ, dK, dVt: fp32 gradients, fully overwritten.
+ * Launches, in stream order: row terms, key pass (dK, dV^T, dS), dQ pass.
+ */
+sa_status sa_backward(const void* dO, const void* O, const float* L, float* D,
+                      void* dS, size_t dS_bytes,
+                      const void* Q, const void* K, const void* Vt, float c, float s,
+                      int T, int heads, int kv_heads,
+                      float* dQ, float* dK, float* dVt, void* stream);
+
+/* Backward for a general shape; arguments as sa_backward. */
+sa_status sa_backward_ex(const sa_shape* shape, const void* dO, const void* O, const float* L,
+                         float* D, void* dS, size_t dS_bytes,
+                         const void* Q, const void* K, const void* Vt, float c, float s,
+                         float* dQ, float* dK, float* dVt, void* stream);
+
+/*
+ * The backward's three launches, one at a time, for measurement and tests.
+ * sa_backward_ex is exactly these three calls in this order.
+ *
+ * Row terms (StreamingAttentionSM86 page, banner "The query pass split in
+ * two around the key pass", the row terms): D = rowsum(dO * O), binary32,
+ * 0 on padded rows.
+ */
+sa_status sa_row_terms(const sa_shape* shape, const void* dO, const void* O, float* D, void* stream);
+
+/*
+ * Key pass (same page, banner "The key launch"; it also stores the score
+ * gradients, per the split query pass's banner): for every 64-key tile,
+ * recompute S, P and dP for every later query, accumulate dK and dV over the
+ * group's heads and store dS (fp16, the words the dK product uses) into the
+ * workspace, exact zeros where masked.
+ */
+sa_status sa_key_pass(const sa_shape* shape, const void* Q, const void* K, const void* Vt,
+                      const void* dO, const float* L, const float* D, void* dS, size_t dS_bytes,
+                      float c, float s, float* dK, float* dVt, void* stream);
+
+/*
+ * dQ pass (same page, split query pass, dQ from stored dS): for each query
+ * tile, dQ = s * sum over key tiles up to the diagonal of dS K.
+ * The workspace must hold a key pass's dS for the same shape.
+ */
+sa_status sa_dq_pass(const sa_shape* shape, const void* K, const void* dS, size_t dS_bytes, float s,
+                     float* dQ, void* stream);
+
+/* Static text for a status value ("unknown status" for anything else). */
+const char* sa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SA_H */

@@ -1,0 +1,151 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads, exports
+every function include/sa.h declares, and rejects bad shapes, pointers,
+workspace sizes and scales with the documented status before launching
+anything.  Only error paths are called here; no call reaches a kernel."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import causal_streaming_attention_amd as sa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sa.LIB_PATH):
+        from causal_streaming_attention_amd import build
+        build.build()
+    return sa.native()
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(sa.exported_symbols())
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", sa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (sa_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_header_compiles_as_plain_c(tmp_path):
+    src = tmp_path / "use.c"
+    src.write_text('#include "sa.h"\nint main(void) { sa_shape s = {1, 64, 1, 1, 1, 0, 0};'
+                   ' return (int)sa_backward_workspace_bytes(&s) == 0; }\n')
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-c", str(src), "-I", os.path.join(ROOT, "include"),
+                        "-o", str(tmp_path / "use.o")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def shape(batch=1, T=128, heads=4, kv=2, causal=1, order=0, seqlens=None):
+    return sa.SaShape(batch, T, heads, kv, causal, seqlens, order)
+
+
+@pytest.mark.parametrize("kw,ok", [
+    ({}, True),
+    ({"T": 64}, True),
+    ({"T": 0}, False),
+    ({"T": 96}, False),
+    ({"T": 100}, False),
+    ({"T": 1 << 21}, False),
+    ({"batch": 0}, False),
+    ({"heads": 0}, False),
+    ({"kv": 0}, False),
+    ({"heads": 6, "kv": 4}, False),
+    ({"heads": 65536, "kv": 1}, False),
+    ({"heads": 32, "kv": 8}, True),
+    ({"causal": 2}, False),
+    ({"order": 2}, False),
+    ({"order": 1}, True),
+    ({"batch": 1 << 20, "heads": 32, "kv": 8}, False),
+])
+def test_admission(lib, kw, ok):
+    st = sa.sa_check_shape(shape(**kw))
+    assert st == (sa.SA_OK if ok else sa.SA_ERR_SHAPE), sa.sa_status_string(st)
+
+
+def test_admission_null_and_misaligned_seqlens(lib):
+    assert lib.sa_check_shape(None) == sa.SA_ERR_NULL
+    assert sa.sa_check_shape(shape(seqlens=0x1002)) == sa.SA_ERR_ALIGN
+
+
+def test_workspace_bytes(lib):
+    nt = 4096 // 64
+    assert sa.sa_backward_workspace_bytes(shape(1, 4096, 32, 8, 1)) == 32 * nt * (nt + 1) // 2 * 8192
+    assert sa.sa_backward_workspace_bytes(shape(16, 2048, 16, 16, 0)) == 16 * 16 * 32 * 32 * 8192
+    assert sa.sa_backward_workspace_bytes(shape(T=96)) == 0
+
+
+FAKE = 0x10000  # an aligned address that is never dereferenced: every call below fails first
+
+
+def test_forward_rejects_null_misaligned_and_bad_scale(lib):
+    s = shape()
+    args = [FAKE] * 5
+    for i in range(5):
+        bad = list(args)
+        bad[i] = None
+        assert lib.sa_forward_ex(ctypes.byref(s), *bad, 0.18, None) == sa.SA_ERR_NULL
+        bad[i] = FAKE + 8
+        assert lib.sa_forward_ex(ctypes.byref(s), *bad, 0.18, None) == sa.SA_ERR_ALIGN
+    for c in (0.0, -1.0, float("inf"), float("nan")):
+        assert lib.sa_forward_ex(ctypes.byref(s), *args, c, None) == sa.SA_ERR_ARGUMENT
+    assert lib.sa_forward(*args, 0.18, 96, 4, 2, None) == sa.SA_ERR_SHAPE
+    assert lib.sa_forward(None, *args[1:], 0.18, 128, 4, 2, None) == sa.SA_ERR_NULL
+
+
+def test_backward_rejects_bad_arguments(lib):
+    s = shape()
+    need = sa.sa_backward_workspace_bytes(s)
+    ptrs = [FAKE] * 11   # dO O L D dS Q K Vt dQ dK dVt
+
+    def call(p, ws=need, c=0.18, sc=0.125, sh=s):
+        return lib.sa_backward_ex(ctypes.byref(sh), p[0], p[1], p[2], p[3], p[4], ws, p[5], p[6], p[7], c, sc,
+                                  p[8], p[9], p[10], None)
+
+    for i in range(11):
+        bad = list(ptrs)
+        bad[i] = None
+        assert call(bad) == sa.SA_ERR_NULL
+        bad[i] = FAKE + 4
+        assert call(bad) == sa.SA_ERR_ALIGN
+    assert call(ptrs, ws=need - 1) == sa.SA_ERR_WORKSPACE
+    assert call(ptrs, sc=0.0) == sa.SA_ERR_ARGUMENT
+    assert call(ptrs, c=float("nan")) == sa.SA_ERR_ARGUMENT
+    assert call(ptrs, sh=shape(heads=3, kv=2)) == sa.SA_ERR_SHAPE
+    assert lib.sa_backward(*ptrs[:5], need, *ptrs[5:8], 0.18, 0.125, 100, 4, 2, *ptrs[8:], None) == sa.SA_ERR_SHAPE
+
+
+def test_stage_entry_points_reject_bad_arguments(lib):
+    s = shape()
+    need = sa.sa_backward_workspace_bytes(s)
+    assert lib.sa_row_terms(ctypes.byref(s), FAKE, None, FAKE, None) == sa.SA_ERR_NULL
+    assert lib.sa_key_pass(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 2, 0.18, 0.125,
+                           FAKE, FAKE, None) == sa.SA_ERR_WORKSPACE
+    assert lib.sa_dq_pass(ctypes.byref(s), FAKE, FAKE, need, -0.125, FAKE, None) == sa.SA_ERR_ARGUMENT
+    assert lib.sa_dq_pass(ctypes.byref(s), FAKE, FAKE + 1, need, 0.125, FAKE, None) == sa.SA_ERR_ALIGN
+
+
+def test_status_strings(lib):
+    for st in range(7):
+        assert sa.sa_status_string(st)
+    assert sa.sa_status_string(99) == "unknown status"
+
+
+def test_base2_scale_is_the_nearest_binary32():
+    import struct
+    c = sa.base2_scale(0.125)
+    assert struct.pack(">f", c).hex() == "3e38aa3b"

@@ -1,0 +1,197 @@
+"""GPU parity: the HIP path (through the C ABI) against the binary64 oracle.
+
+Small problems compare every output; the five named workloads run at their
+full sizes in the launch configuration the benchmark times and compare rows
+and key columns the oracle computes one by one, plus properties that hold at
+any size.  Also: bitwise determinism across repeats and block orders, grouped
+heads against repeated heads, variable length against per-sequence runs, and
+padding that holds garbage."""
+import numpy as np
+import pytest
+
+import oracle
+from causal_streaming_attention_amd.workloads import SCALE, WORKLOADS, generate, make_inputs
+from parity_util import (check_forward, check_grad, full_reference, rel_l2, run_gpu, sample_cols, sample_rows,
+                         say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_all(inputs, causal, where, block_order=0):
+    _, got = run_gpu(inputs, causal, block_order=block_order)
+    ref = full_reference(inputs, causal)
+    check_forward(got["O"], got["L"], ref["O"], ref["L"], where)
+    errs = {k: check_grad(k, got[k], ref[k], where) for k in ("dQ", "dK", "dVt")}
+    # padded rows / keys are exact zeros
+    if inputs["seqlens"] is not None:
+        for b, n in enumerate(inputs["seqlens"]):
+            assert np.all(got["D"][b, :, n:] == 0) and np.all(got["dQ"][b, :, n:] == 0), where
+            assert np.all(got["dK"][b, :, n:] == 0) and np.all(got["dVt"][b, :, :, n:] == 0), where
+    d_err = rel_l2(got["D"], ref["D"])
+    assert d_err <= 1e-2, f"{where}: D rel L2 {d_err:.2e}"
+    say(f"{where}: dQ {errs['dQ']:.2e} dK {errs['dK']:.2e} dV {errs['dVt']:.2e}")
+    return got
+
+
+SMALL = [
+    # name, B, T, H, KV, causal, seqlens
+    ("mha_t128_causal", 1, 128, 1, 1, True, None),
+    ("gqa2_t320_causal_odd_tiles", 2, 320, 4, 2, True, None),
+    ("gqa3_t192_causal", 1, 192, 6, 2, True, None),
+    ("gqa8_t256_causal", 1, 256, 8, 1, True, None),
+    ("mha_t128_full", 1, 128, 2, 2, False, None),
+    ("varlen_full_b3_t256", 3, 256, 2, 2, False, [0, 1, 200]),
+    ("varlen_causal_b4_t192", 4, 192, 4, 2, True, [65, 64, 130, 191]),
+    ("varlen_gqa4_full_b2_t384", 2, 384, 4, 1, False, [383, 97]),
+]
+
+
+@pytest.mark.parametrize("name,B,T,H,KV,causal,seqlens", SMALL, ids=[c[0] for c in SMALL])
+def test_small_full_parity(name, B, T, H, KV, causal, seqlens):
+    say(f"case {name}")
+    x = make_inputs(B, T, H, KV, seed=100 + T + H, seqlens=seqlens)
+    _check_all(x, causal, name)
+
+
+def test_tiny_causal_t128_workload():
+    w = WORKLOADS["tiny_causal_t128"]
+    say(f"case {w.name}")
+    _check_all(generate(w), w.causal, w.name)
+
+
+def test_causal_mha_t1024_workload():
+    w = WORKLOADS["causal_mha_t1024"]
+    say(f"case {w.name}")
+    _check_all(generate(w), w.causal, w.name)
+
+
+def _sampled(w, n_rows, n_cols, kv_list, col_lo=0):
+    x = generate(w)
+    say(f"case {w.name}: gpu")
+    buf, got = run_gpu(x, w.causal)
+    B, H, T, KV = w.batch, w.heads, w.T, w.kv_heads
+    rows = sample_rows(B, H, T, n_rows, seed=w.seed)
+    say(f"case {w.name}: oracle rows {rows.size}")
+    D, dQ, O, L = oracle.backward_rows(x["Q"], x["K"], x["Vt"], x["dO"], s=SCALE, causal=w.causal,
+                                       seqlens=x["seqlens"], rows=rows)
+    check_forward(got["O"].reshape(-1, 64)[rows], got["L"].reshape(-1)[rows], O, L, w.name)
+    check_grad("dQ", got["dQ"].reshape(-1, 64)[rows], dQ, w.name)
+    assert rel_l2(got["D"].reshape(-1)[rows], D) <= 1e-2
+    cols = sample_cols(B, KV, T, n_cols, seed=w.seed + 1, kv_list=kv_list, lo=col_lo)
+    say(f"case {w.name}: oracle cols {cols.size}")
+    dK, dV = oracle.backward_cols(x["Q"], x["K"], x["Vt"], x["dO"], s=SCALE, causal=w.causal,
+                                  seqlens=x["seqlens"], cols=cols)
+    check_grad("dK", got["dK"].reshape(-1, 64)[cols], dK, w.name)
+    check_grad("dV", np.swapaxes(got["dVt"], -1, -2).reshape(-1, 64)[cols], dV, w.name)
+    return x, got
+
+
+def _gradient_sums(x, got, w):
+    """sum_j dK_j = 0 and sum_j dV_j = sum of the group's admitted dO rows, at full size."""
+    dO = x["dO"].astype(np.float64)
+    G = w.heads // w.kv_heads
+    lens = x["seqlens"] if x["seqlens"] is not None else [w.T] * w.batch
+    for b in range(w.batch):
+        n = int(lens[b])
+        for kv in range(w.kv_heads):
+            want = dO[b, kv * G:(kv + 1) * G, :n].sum(axis=(0, 1))
+            got_v = got["dVt"][b, kv].sum(axis=1)
+            assert np.max(np.abs(got_v - want)) <= 1e-2 * max(1.0, np.max(np.abs(want))), (b, kv)
+            dk = got["dK"][b, kv]          # [T, 64]; sum over keys vanishes up to rounding
+            assert np.all(np.abs(dk.sum(axis=0)) <= 1e-2 * np.sqrt(np.sum(dk * dk, axis=0)) + 1e-6), (b, kv)
+
+
+def test_causal_gqa_t4096_workload_sampled():
+    w = WORKLOADS["causal_gqa_t4096"]
+    x, got = _sampled(w, 384, 160, kv_list=[0, 7])
+    _gradient_sums(x, got, w)
+
+
+def test_varlen_b16_t2048_workload_sampled():
+    w = WORKLOADS["varlen_b16_t2048"]
+    x, got = _sampled(w, 384, 128, kv_list=[3])
+    lens = x["seqlens"]
+    for b, n in enumerate(lens):
+        assert np.all(got["O"][b, :, n:] == 0) and np.all(np.isneginf(got["L"][b, :, n:]))
+        assert np.all(got["dQ"][b, :, n:] == 0) and np.all(got["dK"][b, :, n:] == 0)
+    _gradient_sums(x, got, w)
+
+
+def test_long_causal_gqa_t16384_workload_sampled():
+    w = WORKLOADS["long_causal_gqa_t16384"]
+    # key columns from the last 768 keys: their gradients need only the rows after them
+    x, got = _sampled(w, 256, 96, kv_list=[5], col_lo=w.T - 768)
+    _gradient_sums(x, got, w)
+
+
+def test_determinism_and_block_order():
+    w = WORKLOADS["causal_gqa_t4096"]
+    say("case determinism")
+    x = generate(w)
+    _, a = run_gpu(x, True, block_order=0)
+    _, b = run_gpu(x, True, block_order=0)
+    _, c = run_gpu(x, True, block_order=1)
+    for k in a:
+        assert np.array_equal(a[k], b[k], equal_nan=True), f"{k} differs between repeats"
+        assert np.array_equal(a[k], c[k], equal_nan=True), f"{k} differs between block orders"
+
+
+def test_grouped_heads_equal_repeated_heads():
+    say("case gqa-vs-mha")
+    x = make_inputs(1, 256, 8, 2, seed=21)
+    G = 4
+    xm = dict(x, K=np.repeat(x["K"], G, axis=1), Vt=np.repeat(x["Vt"], G, axis=1))
+    _, g = run_gpu(x, True)
+    _, m = run_gpu(xm, True)
+    for k in ("O", "L", "D", "dQ"):
+        assert np.array_equal(g[k], m[k]), k
+    for k in ("dK", "dVt"):
+        summed = m[k].reshape(1, 2, G, *m[k].shape[2:]).sum(axis=2)
+        assert rel_l2(g[k], summed) <= 1e-5, k
+
+
+def test_varlen_equals_per_sequence_runs():
+    say("case varlen-vs-single")
+    lens = [130, 64, 1, 250]
+    x = make_inputs(4, 256, 4, 2, seed=22, seqlens=lens)
+    for causal in (False, True):
+        _, got = run_gpu(x, causal)
+        for b, n in enumerate(lens):
+            Tp = ((n + 63) // 64) * 64
+            one = {k: x[k][b:b + 1, :, :Tp] for k in ("Q", "K", "dO")}
+            one["Vt"] = x["Vt"][b:b + 1, :, :, :Tp]
+            one["seqlens"] = np.array([n], dtype=np.int32)
+            _, r = run_gpu(one, causal)
+            for k in ("O", "L", "D", "dQ", "dK"):
+                assert np.array_equal(got[k][b:b + 1, :, :Tp], r[k]), (causal, b, k)
+            assert np.array_equal(got["dVt"][b:b + 1, :, :, :Tp], r["dVt"]), (causal, b)
+
+
+def test_padding_garbage_does_not_leak():
+    say("case padding-garbage")
+    lens = [100, 37, 192]
+    x = make_inputs(3, 192, 4, 2, seed=23, seqlens=lens)
+    for causal in (False, True):
+        _, clean = run_gpu(x, causal)
+        dirty = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in x.items()}
+        rng = np.random.default_rng(0)
+        for b, n in enumerate(lens):
+            for k in ("Q", "K", "dO"):
+                pad = dirty[k][b, :, n:]
+                pad[...] = rng.choice([-65504.0, 65504.0], size=pad.shape).astype(np.float16)
+            pad = dirty["Vt"][b, :, :, n:]
+            pad[...] = rng.choice([-65504.0, 65504.0], size=pad.shape).astype(np.float16)
+        _, got = run_gpu(dirty, causal)
+        for k in clean:
+            assert np.array_equal(clean[k], got[k]), (causal, k)
+
+
+def test_row_terms_from_the_forward_output():
+    """D is rowsum(dO * O) of the forward's own fp16 O, to binary32 accuracy."""
+    say("case row-terms")
+    x = make_inputs(2, 256, 4, 4, seed=24, seqlens=[256, 77])
+    buf, got = run_gpu(x, True)
+    O16 = buf.O.view(2, 256, 4, 64).permute(0, 2, 1, 3).float().cpu().numpy().astype(np.float64)
+    want = np.sum(x["dO"].astype(np.float64) * O16, axis=-1)
+    want[1, :, 77:] = 0.0
+    assert np.max(np.abs(got["D"] - want)) <= 1e-5 * max(1.0, np.max(np.abs(want)))
