@@ -1,0 +1,206 @@
+"""Benchmark: causal attention forward + backward TFLOP/s (fp16 inputs, fp32
+accumulation, head width 64) on one MI355X, and the fraction of the fp16
+dense MFMA peak.
+
+One step is one pass of the whole path over one batch of synthetic input:
+forward (sa_forward_ex), then the backward's row terms, key pass and dQ pass
+(the three launches of sa_backward_ex, issued one by one so each can be timed).
+Inputs are resident in HBM before the timed region starts.
+
+FLOPs are algorithmic: per admitted (query, key) pair and query head, the
+forward's two products cost 4 * 64 and the backward's five cost 10 * 64; a
+causal square counts T^2 / 2 pairs.
+
+Prints ONE JSON line.  With --gpus above 1 it exits: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal attn fwd+bwd TFLOP/s (fp16, d=64) and % of MFMA fp16 peak"
+# MI355X dense fp16 MFMA: 256 CUs x 2.4 GHz x 4096 FLOP/clock/CU (the published 2.5 PFLOP/s).
+PEAK_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
+HBM_PEAK_GBS = 8000.0
+HEAD_DIM = 64
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "causal_streaming_attention_amd", "csrc", f)
+                  for f in ("sa_device.h", "sa_forward.hip", "sa_backward.hip")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def pairs_per_head(w, seqlens):
+    """Admitted (query, key) pairs per query head, summed over the batch."""
+    if seqlens is not None:
+        sq = float(np.sum(np.asarray(seqlens, dtype=np.float64) ** 2))
+        return sq * (0.5 if w.causal else 1.0)
+    return w.batch * float(w.T) * w.T * (0.5 if w.causal else 1.0)
+
+
+def kernel_flops(w, seqlens):
+    p = pairs_per_head(w, seqlens) * w.heads
+    return {"forward": 4 * HEAD_DIM * p, "key_pass": 8 * HEAD_DIM * p, "dq_pass": 2 * HEAD_DIM * p,
+            "row_terms": 0.0, "total": 14 * HEAD_DIM * p}
+
+
+def row_terms_bytes(w):
+    rows = w.batch * w.heads * w.T
+    return rows * (HEAD_DIM * 2 * 2 + 4)   # dO and O fp16 rows in, D fp32 out
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters for this kernel source, else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash() or t.get("workload") != workload:
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x):
+    """Time the binary64 oracle on the first K/V head group (its G query heads, first
+    sequence) of the same inputs: the whole forward and backward of that group, i.e.
+    1 / (batch * kv_heads) of the job, reported in the workload's FLOP convention."""
+    import oracle
+    from causal_streaming_attention_amd.workloads import SCALE
+    G = w.heads // w.kv_heads
+    sl = None if x["seqlens"] is None else x["seqlens"][:1]
+    part = {"Q": x["Q"][:1, :G], "K": x["K"][:1, :1], "Vt": x["Vt"][:1, :1], "dO": x["dO"][:1, :G]}
+    t0 = time.perf_counter()
+    oracle.backward(part["Q"], part["K"], part["Vt"], part["dO"], s=SCALE, causal=w.causal, seqlens=sl)
+    dt = time.perf_counter() - t0
+    n = w.T if sl is None else int(sl[0])
+    flops = 14 * HEAD_DIM * (n * float(n) * (0.5 if w.causal else 1.0)) * G
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"one K/V head group ({G} query heads, batch 1, T={w.T}) of {w.name}: full forward "
+                      f"and backward, {flops / 1e9:.2f} GFLOP in {dt:.1f} s (1/{w.batch * w.kv_heads} of the job)",
+            "cpu": platform.processor() or _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="causal_gqa_t4096")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--block-order", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the sharding plan is design only)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import causal_streaming_attention_amd as sa
+    from causal_streaming_attention_amd.workloads import SCALE, WORKLOADS, generate
+
+    w = WORKLOADS[args.workload]
+    x = generate(w)
+    buf = sa.Buffers(x, w.causal, block_order=args.block_order)
+    c = sa.base2_scale(SCALE)
+    sh = buf.shape
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        sa.sa_forward_ex(sh, buf.Q, buf.K, buf.Vt, buf.O, buf.L, c, stream)
+        if ev: ev[1].record(stream)
+        sa.sa_row_terms(sh, buf.dO, buf.O, buf.D, stream)
+        if ev: ev[2].record(stream)
+        sa.sa_key_pass(sh, buf.Q, buf.K, buf.Vt, buf.dO, buf.L, buf.D, buf.dS, buf.ws_bytes, c, SCALE, buf.dK,
+                       buf.dVt, stream)
+        if ev: ev[3].record(stream)
+        sa.sa_dq_pass(sh, buf.K, buf.dS, buf.ws_bytes, SCALE, buf.dQ, stream)
+        if ev: ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    names = ["forward", "row_terms", "key_pass", "dq_pass"]
+    per = {n: float(np.mean([events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps)]))
+           for i, n in enumerate(names)}
+    step_ms = float(np.mean([events[k][0].elapsed_time(events[k][4]) for k in range(args.steps)]))
+    ms_per_step = max(step_ms, wall * 1e3 / args.steps)
+    fl = kernel_flops(w, x["seqlens"])
+    value = fl["total"] / (ms_per_step * 1e-3) / 1e12
+
+    dominant = max(("forward", "key_pass", "dq_pass"), key=lambda n: per[n])
+    achieved = fl[dominant] / (per[dominant] * 1e-3) / 1e12
+    traffic = load_traffic(dominant, w.name)
+    roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2), "peak": round(PEAK_TFLOPS, 1),
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic,
+                "algorithmic_flops_per_launch": fl[dominant], "avg_launch_ms": round(per[dominant], 4)}
+
+    kernels = {}
+    for n in names:
+        e = {"ms": round(per[n], 4)}
+        if fl[n] > 0:
+            e["tflops"] = round(fl[n] / (per[n] * 1e-3) / 1e12, 1)
+            e["frac_mfma_peak"] = round(fl[n] / (per[n] * 1e-3) / 1e12 / PEAK_TFLOPS, 4)
+        else:
+            gbs = row_terms_bytes(w) / (per[n] * 1e-3) / 1e9
+            e["gb_per_s"] = round(gbs, 1)
+            e["frac_hbm_peak"] = round(gbs / HBM_PEAK_GBS, 4)
+        kernels[n] = e
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.T, "heads": w.heads, "kv_heads": w.kv_heads,
+                   "head_dim": HEAD_DIM, "causal": w.causal, "varlen": w.varlen, "parallelism": "single GPU"},
+        "pct_mfma_peak": round(100 * value / PEAK_TFLOPS, 2),
+        "flops_per_step": fl["total"],
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -63,35 +63,58 @@ __global__ __launch_bounds__(kRowThreads) void sa_row_terms_kernel(const half_t*
 
 // ---------------------------------------------------------------------------
 // Key pass.  One workgroup per (batch, K/V head, 64-key tile kt); 2 GW waves:
-// wave pair `slot` takes query heads kv G + slot, + GW, ... of the group in
-// turn, and within a pair each wave owns 32 of the tile's keys.  Each pair
-// walks its head's 32-query sub-tiles from the last down to the diagonal one
-// (the pages' order), staging Q, dO, L and D of the sub-tile in LDS
-// (double-buffered).  Per sub-tile and wave:
+// wave (slot, khalf) takes query heads kv G + slot, + GW, ... of the group in
+// turn and owns keys kt * 64 + 32 khalf + 0..31.  Each wave walks its head's
+// 32-query sub-tiles from the last down to the diagonal one (the pages'
+// order) on its own: it stages each sub-tile's Q, dO, L and D into a private
+// LDS double buffer with direct global-to-LDS loads, one sub-tile ahead, so
+// the loop has no workgroup barrier and the waves sharing a SIMD drift apart
+// and overlap their matrix and vector work.  Per sub-tile and wave:
 //   S  = Q K^T  (A = Q rows, LDS; B = K^T, registers)
 //   dP = dO V^T (A = dO rows, LDS; B = V^T, registers, transposed once)
 //   P  = 2^(S c - L),  dS = P (dP - D)  -- in registers, lane = key
 //   dS stored as fp16 (the words of dK's product) into its 64x64 tile
 //   dV^T += dO^T P, dK^T += Q^T dS (A = dO^T / Q^T by transposed LDS
 //   reads, in the permuted query order of P's / dS's accumulators).
-// The pairs' dK and dV are then summed through LDS in slot order, dK scaled
+// The slots' dK and dV are then summed through LDS in slot order, dK scaled
 // by s, and stored with coalesced 16-byte writes.
+//
+// A staged 32 x 64 fp16 sub-tile has 128-byte rows whose 16-byte chunk c of
+// row r sits at chunk c ^ (r % 8): the eight rows a 16-lane read touches fall
+// in distinct banks without padding (which direct loads cannot make).
 // ---------------------------------------------------------------------------
 constexpr int kSubRows = 32;
-constexpr int kSubHalves = kSubRows * kLdsRow;
-constexpr int kSlotBufBytes = 2 * kSubHalves * 2 + 2 * kSubRows * 4;  // Q, dO, L, D
-constexpr int kRedRow = 68;                                             // floats
+constexpr int kSubBytes = kSubRows * kHeadDim * 2;          // 4096
+constexpr int kItemBytes = 2 * kSubBytes + 2 * kSubRows * 4;  // Q, dO, L, D: 8448
+constexpr int kDsxRow = 36;                                   // halves: 32 queries + pad
+constexpr int kDsxBytes = 32 * kDsxRow * 2;                  // one wave's 32x32 dS block
+constexpr int kWaveBytes = 2 * kItemBytes + kDsxBytes;
+constexpr int kRedRow = 68;                                  // floats
 
 template <int GW>
 struct KeyLds {
-    static constexpr int stage = GW * 2 * kSlotBufBytes;
+    static constexpr int stage = 2 * GW * kWaveBytes;        // per wave: two items and a dS block
     static constexpr int red = GW * 64 * kRedRow * 4;
     static constexpr int vt = 64 * kLdsRow * 2;
     static constexpr int bytes = stage > red ? (stage > vt ? stage : vt) : (red > vt ? red : vt);
 };
 
+// Element offset of (row, col) in a swizzled 32 x 64 sub-tile.
+__device__ __forceinline__ int swz(int row, int col) {
+    return row * kHeadDim + ((((col >> 3) ^ row) & 7) << 3) + (col & 7);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma16(const void* g, char* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)((__attribute__((address_space(3))) char*)lds_wave_base), 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, char* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)((__attribute__((address_space(3))) char*)lds_wave_base), 4, 0, 0);
+}
+
 template <bool CAUSAL, bool VARLEN, int GW>
-__global__ __launch_bounds__(128 * GW, 1) void sa_key_kernel(
+__global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     const half_t* __restrict__ Q, const half_t* __restrict__ K, const half_t* __restrict__ Vt,
     const half_t* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ D,
     half_t* __restrict__ dS, float* __restrict__ dK, float* __restrict__ dVt,
@@ -100,9 +123,9 @@ __global__ __launch_bounds__(128 * GW, 1) void sa_key_kernel(
     constexpr int kThreads = 128 * GW;
     __shared__ __attribute__((aligned(16))) char smem[KeyLds<GW>::bytes];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int l32 = lane & 31, hi = lane >> 5;
-    const int slot = wave >> 1, khalf = wave & 1, st = tid & 127;
+    const int slot = wave >> 1, khalf = wave & 1;
 
     int kt, bkv;
     if (block_order == 0) {  // key tile 0 first: it walks every query
@@ -154,144 +177,155 @@ __global__ __launch_bounds__(128 * GW, 1) void sa_key_kernel(
         __syncthreads();
     }
 
-    f32x16 dkacc[2] = {zero16(), zero16()}, dvacc[2] = {zero16(), zero16()};
+    f32x16 dkacc0 = zero16(), dkacc1 = zero16(), dvacc0 = zero16(), dvacc1 = zero16();
 
-    // Staging of one item (head iteration gi, sub-tile sub) by the slot's 128 threads.
-    uint4 qreg[2], oreg[2], lreg;
+    char* const wstage = smem + wave * kWaveBytes;  // this wave's two item buffers
+    half_t* const dsx = (half_t*)(wstage + 2 * kItemBytes);  // and its dS block [key][query]
+    const int dma_row = lane >> 3;                         // + 8 u
     auto item_head = [&](int it) { return kv * G + (it / n_sub) * GW + slot; };
     auto item_sub = [&](int it) { return sub_hi - 1 - (it % n_sub); };
-    auto load_item = [&](int it) {
+    // Direct loads of one item into buffer `buf`: 4 x 1 KB of Q rows, 4 x 1 KB
+    // of dO rows (lane l of load u: row 8 u + l / 8, stored chunk l % 8 holding
+    // the row's chunk (l % 8) ^ (row % 8)), then L (lanes 0..31) and D (32..63).
+    auto issue_item = [&](int it, int buf) {
         const int head = item_head(it), sub = item_sub(it);
-        const size_t rowbase = (((size_t)b * H + head) * T + (size_t)sub * kSubRows);
+        const size_t rowbase = ((size_t)b * H + head) * T + (size_t)sub * kSubRows;
+        char* base = wstage + buf * kItemBytes;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            int chunk = st + 128 * u, row = chunk >> 3, col = (chunk & 7) * 8;
-            qreg[u] = *(const uint4*)(Q + (rowbase + row) * kHeadDim + col);
-            oreg[u] = *(const uint4*)(dO + (rowbase + row) * kHeadDim + col);
+        for (int u = 0; u < 4; ++u) {
+            const int row = 8 * u + dma_row;
+            const int col = (((lane & 7) ^ row) & 7) * 8;
+            const size_t off = (rowbase + row) * kHeadDim + col;
+            dma16(Q + off, base + 1024 * u);
+            dma16(dO + off, base + kSubBytes + 1024 * u);
         }
-        if (st < 16) {
-            const float* src = (st < 8) ? L : D;
-            lreg = *(const uint4*)(src + rowbase + 4 * (st & 7));
-        }
-    };
-    auto store_item = [&](int it, int buf) {
-        const int sub = item_sub(it);
-        char* sb = smem + (slot * 2 + buf) * kSlotBufBytes;
-        half_t* Qs = (half_t*)sb;
-        half_t* dOs = Qs + kSubHalves;
-        float* LDs = (float*)(dOs + kSubHalves);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            int chunk = st + 128 * u, row = chunk >> 3, col = (chunk & 7) * 8;
-            uint4 qv = qreg[u], ov = oreg[u];
-            if (VARLEN && sub * kSubRows + row >= len) {  // padded rows never reach dK or dV
-                qv = make_uint4(0, 0, 0, 0);
-                ov = make_uint4(0, 0, 0, 0);
-            }
-            *(uint4*)&Qs[row * kLdsRow + col] = qv;
-            *(uint4*)&dOs[row * kLdsRow + col] = ov;
-        }
-        if (st < 16) {
-            uint4 v = lreg;
-            if (VARLEN) {
-                int r0 = sub * kSubRows + 4 * (st & 7);
-                unsigned* e = (unsigned*)&v;
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    if (r0 + t >= len) e[t] = 0u;
-            }
-            *(uint4*)&LDs[(st < 8 ? 0 : kSubRows) + 4 * (st & 7)] = v;
-        }
+        const float* src = (lane < 32) ? (L + rowbase + lane) : (D + rowbase + (lane - 32));
+        dma4(src, base + 2 * kSubBytes);
     };
 
-    if (n_items > 0) {
-        load_item(0);
-        store_item(0, 0);
-    }
-    __syncthreads();
+    if (n_items > 0) issue_item(0, 0);
 
     for (int it = 0; it < n_items; ++it) {
         const int buf = it & 1;
-        if (it + 1 < n_items) load_item(it + 1);
-
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this item has landed in LDS
         const int head = item_head(it), sub = item_sub(it);
         const int qb = sub * kSubRows;
-        const char* sb = smem + (slot * 2 + buf) * kSlotBufBytes;
-        const half_t* Qs = (const half_t*)sb;
-        const half_t* dOs = Qs + kSubHalves;
-        const float* Ls = (const float*)(dOs + kSubHalves);
+        half_t* Qs = (half_t*)(wstage + buf * kItemBytes);
+        half_t* dOs = Qs + kSubRows * kHeadDim;
+        float* Ls = (float*)(dOs + kSubRows * kHeadDim);
         const float* Ds = Ls + kSubRows;
-        // This wave's 32x32 block of the 64x64 dS^T tile [key][query].
+        if (VARLEN && qb + kSubRows > len) {
+            // Rows at or past the length never reach dK or dV: clear them.
+            const int keep = max(len - qb, 0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int row = 8 * u + dma_row;
+                if (row >= keep) {
+                    *(uint4*)(Qs + row * kHeadDim + (lane & 7) * 8) = make_uint4(0, 0, 0, 0);
+                    *(uint4*)(dOs + row * kHeadDim + (lane & 7) * 8) = make_uint4(0, 0, 0, 0);
+                }
+            }
+            if ((lane & 31) >= keep) Ls[lane] = 0.0f;  // L (lanes 0..31) and D (32..63)
+        }
+        if (it + 1 < n_items) issue_item(it + 1, buf ^ 1);
+
+        // This wave's 32x32 block of the 64x64 dS tile: quadrant (query half
+        // sub % 2, key half khalf), stored as [key octet 4][query 32][8 keys].
         const int qt = sub >> 1;
         const size_t tile = CAUSAL ? (size_t)qt * (qt + 1) / 2 + kt : (size_t)qt * (T / kTile) + kt;
         half_t* dsp = dS + (((size_t)b * H + head) * (size_t)tiles_per_head + tile) * (kTile * kTile) +
-                      (size_t)(32 * khalf + l32) * kTile + 32 * (sub & 1) + 4 * hi;
+                      (size_t)(2 * (sub & 1) + khalf) * 1024 + 8 * lane;
 
         const bool all_masked = (CAUSAL && qb + kSubRows - 1 < kbase) ||
                                 (VARLEN && (qb >= len || kbase >= len));
         if (all_masked) {
-            const half4 z = {(half_t)0.0f, (half_t)0.0f, (half_t)0.0f, (half_t)0.0f};
+            *(uint4*)dsp = make_uint4(0, 0, 0, 0);
+            *(uint4*)(dsp + 512) = make_uint4(0, 0, 0, 0);
+            continue;
+        }
+        f32x16 sacc = zero16(), pacc = zero16();
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) *(half4*)(dsp + 8 * rg) = z;
-        } else {
-            f32x16 sacc = zero16(), pacc = zero16();
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int off = swz(l32, 16 * q4 + 8 * hi);
+            sacc = mfma32(*(const half8*)(Qs + off), kf[q4], sacc);
+            pacc = mfma32(*(const half8*)(dOs + off), vf[q4], pacc);
+        }
+        const bool need_mask = (CAUSAL && qb < kbase + 31) || (VARLEN && (qb + kSubRows > len || kbase + 32 > len));
+        uint32_t wp[8], wd[8];  // P and dS packed as binary16 pairs, accumulator order
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                half8 aq = *(const half8*)(Qs + l32 * kLdsRow + 16 * q4 + 8 * hi);
-                sacc = mfma32(aq, kf[q4], sacc);
+        for (int rg = 0; rg < 4; ++rg) {
+            const f32x4 lv = *(const f32x4*)(Ls + 8 * rg + 4 * hi);
+            const f32x4 dv = *(const f32x4*)(Ds + 8 * rg + 4 * hi);
+            float p[4], g[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * rg + e;
+                p[e] = exp2_fast(__builtin_fmaf(sacc[r], c, -lv[e]));
+                g[e] = p[e] * (pacc[r] - dv[e]);
             }
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                half8 ao = *(const half8*)(dOs + l32 * kLdsRow + 16 * q4 + 8 * hi);
-                pacc = mfma32(ao, vf[q4], pacc);
-            }
-            const bool need_mask = (CAUSAL && qb < kbase + 31) || (VARLEN && (qb + kSubRows > len || kbase + 32 > len));
-            half8 pp[2], pds[2];
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const f32x4 lv = *(const f32x4*)(Ls + 8 * rg + 4 * hi);
-                const f32x4 dv = *(const f32x4*)(Ds + 8 * rg + 4 * hi);
+            if (need_mask) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * rg + e;
-                    float p = exp2_fast(__builtin_fmaf(sacc[r], c, -lv[e]));
-                    float g = p * (pacc[r] - dv[e]);
-                    if (need_mask) {
-                        const int q = qb + 8 * rg + 4 * hi + e;
-                        const bool masked = (CAUSAL && key > q) || (VARLEN && (q >= len || key >= len));
-                        p = masked ? 0.0f : p;
-                        g = masked ? 0.0f : g;
-                    }
-                    pp[r >> 3][r & 7] = to_half(p);
-                    pds[r >> 3][r & 7] = to_half(g);
+                    const int q = qb + 8 * rg + 4 * hi + e;
+                    const bool masked = (CAUSAL && key > q) || (VARLEN && (q >= len || key >= len));
+                    p[e] = masked ? 0.0f : p[e];
+                    g[e] = masked ? 0.0f : g[e];
                 }
             }
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                half4 v;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = pds[rg >> 1][4 * (rg & 1) + e];
-                *(half4*)(dsp + 8 * rg) = v;
-            }
-            // dV^T += dO^T P and dK^T += Q^T dS; k-step ks covers queries
-            // 16 ks + 4 hi + 0..3 and 16 ks + 8 + 4 hi + 0..3.
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-                for (int db = 0; db < 2; ++db) {
-                    half8 ao = cat(lds_read_tr(dOs + tr_offset(lane, 16 * ks, 16 * ks + 4, 32 * db)),
-                                   lds_read_tr(dOs + tr_offset(lane, 16 * ks + 8, 16 * ks + 12, 32 * db)));
-                    dvacc[db] = mfma32(ao, pp[ks], dvacc[db]);
-                    half8 aq = cat(lds_read_tr(Qs + tr_offset(lane, 16 * ks, 16 * ks + 4, 32 * db)),
-                                   lds_read_tr(Qs + tr_offset(lane, 16 * ks + 8, 16 * ks + 12, 32 * db)));
-                    dkacc[db] = mfma32(aq, pds[ks], dkacc[db]);
-                }
-            }
+            wp[2 * rg] = pack_half2(p[0], p[1]);
+            wp[2 * rg + 1] = pack_half2(p[2], p[3]);
+            wd[2 * rg] = pack_half2(g[0], g[1]);
+            wd[2 * rg + 1] = pack_half2(g[2], g[3]);
         }
-
-        if (it + 1 < n_items) store_item(it + 1, buf ^ 1);
-        __syncthreads();
+        // dS to global: through this wave's LDS block [key][query], read back
+        // transposed so that lane l holds 8 consecutive keys of query l % 32,
+        // and stored as two fully coalesced 1 KB runs.
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg)
+            *(uint2*)(dsx + l32 * kDsxRow + 8 * rg + 4 * hi) = make_uint2(wd[2 * rg], wd[2 * rg + 1]);
+        {
+            half4 x0 = lds_read_tr_async(dsx + tr_offset(lane, 0, 8, 0, kDsxRow));
+            half4 x1 = lds_read_tr_async(dsx + tr_offset(lane, 4, 12, 0, kDsxRow));
+            half4 x2 = lds_read_tr_async(dsx + tr_offset(lane, 16, 24, 0, kDsxRow));
+            half4 x3 = lds_read_tr_async(dsx + tr_offset(lane, 20, 28, 0, kDsxRow));
+            lds_wait4(x0, x1, x2, x3);
+            *(half8*)dsp = cat(x0, x1);
+            *(half8*)(dsp + 512) = cat(x2, x3);
+        }
+        const half8 pp0 = half8_from_words(wp[0], wp[1], wp[2], wp[3]);
+        const half8 pp1 = half8_from_words(wp[4], wp[5], wp[6], wp[7]);
+        const half8 pd0 = half8_from_words(wd[0], wd[1], wd[2], wd[3]);
+        const half8 pd1 = half8_from_words(wd[4], wd[5], wd[6], wd[7]);
+        // dV^T += dO^T P and dK^T += Q^T dS; k-step ks covers queries
+        // 16 ks + 4 hi + 0..3 and 16 ks + 8 + 4 hi + 0..3.  Transposed read:
+        // lane l gets column (16 ((l / 16) % 2) + l % 16) of rows row0 + 0..3.
+        const int trr = (lane & 15) >> 2, trc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        half4 t[16];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int ra = 16 * ks + 4 * hi + trr, rb = ra + 8;
+            t[8 * ks + 0] = lds_read_tr_async(dOs + swz(ra, trc));
+            t[8 * ks + 1] = lds_read_tr_async(dOs + swz(rb, trc));
+            t[8 * ks + 2] = lds_read_tr_async(dOs + swz(ra, 32 + trc));
+            t[8 * ks + 3] = lds_read_tr_async(dOs + swz(rb, 32 + trc));
+            t[8 * ks + 4] = lds_read_tr_async(Qs + swz(ra, trc));
+            t[8 * ks + 5] = lds_read_tr_async(Qs + swz(rb, trc));
+            t[8 * ks + 6] = lds_read_tr_async(Qs + swz(ra, 32 + trc));
+            t[8 * ks + 7] = lds_read_tr_async(Qs + swz(rb, 32 + trc));
+        }
+        lds_wait(t[0], t[1], t[2], t[3], t[4], t[5], t[6], t[7]);
+        lds_wait(t[8], t[9], t[10], t[11], t[12], t[13], t[14], t[15]);
+        dvacc0 = mfma32(cat(t[0], t[1]), pp0, dvacc0);
+        dvacc1 = mfma32(cat(t[2], t[3]), pp0, dvacc1);
+        dkacc0 = mfma32(cat(t[4], t[5]), pd0, dkacc0);
+        dkacc1 = mfma32(cat(t[6], t[7]), pd0, dkacc1);
+        dvacc0 = mfma32(cat(t[8], t[9]), pp1, dvacc0);
+        dvacc1 = mfma32(cat(t[10], t[11]), pp1, dvacc1);
+        dkacc0 = mfma32(cat(t[12], t[13]), pd1, dkacc0);
+        dkacc1 = mfma32(cat(t[14], t[15]), pd1, dkacc1);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // every wave is done with its staging buffers
 
     // Group sum through LDS in slot order, then coalesced stores.
     float* red = (float*)smem;
@@ -306,7 +340,7 @@ __global__ __launch_bounds__(128 * GW, 1) void sa_key_kernel(
             *(f32x4*)(row + 32) = v1;
         }
     };
-    to_lds(dkacc[0], dkacc[1]);
+    to_lds(dkacc0, dkacc1);
     __syncthreads();
     for (int idx = tid; idx < 64 * 16; idx += kThreads) {  // dK[key][d]: 16 float4s per key
         const int kk = idx >> 4, d4 = (idx & 15) * 4;
@@ -317,7 +351,7 @@ __global__ __launch_bounds__(128 * GW, 1) void sa_key_kernel(
         *(f32x4*)(dK + (key_row0 + kk) * kHeadDim + d4) = v;
     }
     __syncthreads();
-    to_lds(dvacc[0], dvacc[1]);
+    to_lds(dvacc0, dvacc1);
     __syncthreads();
     for (int idx = tid; idx < 64 * 16; idx += kThreads) {  // dV^T[d][key]: 16 float4s per d row
         const int d = idx >> 4, k4 = (idx & 15) * 4;
@@ -336,11 +370,14 @@ __global__ __launch_bounds__(128 * GW, 1) void sa_key_kernel(
 // ---------------------------------------------------------------------------
 // dQ pass.  One 256-thread workgroup per 128 queries of a query head (two dS
 // tile rows); wave w owns 32 queries.  For each key tile up to the diagonal
-// (the query pass's order), the K tile and the block's two dS^T tiles are
-// staged in LDS (double-buffered) and each wave accumulates
-//   dQ^T += K^T dS^T   (A = K^T, B = dS^T, both by transposed LDS reads),
-// so each lane ends with 4-float runs of one query's dQ row: dQ = s * sum,
-// stored with 16-byte writes.
+// (the query pass's order) the K tile is staged in LDS for the four waves
+// (double-buffered) and each wave accumulates
+//   dQ^T += K^T dS^T   (A = K^T by transposed LDS reads; B = dS^T straight
+//                       from the workspace: its quadrant layout puts the 8
+//                       keys a lane needs for one query in 16 contiguous
+//                       bytes, and a wave's loads in two 512-byte runs)
+// with the next tile's dS loads in flight; each lane ends with 4-float runs of
+// one query's dQ row: dQ = s * sum, stored with 16-byte writes.
 // ---------------------------------------------------------------------------
 constexpr int kDqWaves = 4;
 constexpr int kDqRows = 32 * kDqWaves;
@@ -354,9 +391,9 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
                                                                const int32_t* __restrict__ seqlens, float s,
                                                                int T, int H, int KV, int n_qblk, int BH,
                                                                int block_order, long long tiles_per_head) {
-    __shared__ __attribute__((aligned(16))) half_t lds[2][3][kTileHalvesDq];  // [buf][K | dS row 0 | dS row 1]
+    __shared__ __attribute__((aligned(16))) half_t lds[2][kTileHalvesDq];  // K tiles
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int l32 = lane & 31, hi = lane >> 5;
     int qblk, bh;
     if (block_order == 0) {
@@ -371,102 +408,92 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
     const int len = VARLEN ? min(max(seqlens[b], 0), T) : T;
     const int ntl = VARLEN ? (len + kTile - 1) / kTile : nt;  // dS tile rows/cols in use
     const int qt0 = 2 * qblk;
-    const int qt_w = qt0 + (wave >> 1);
+    const int qt_w = qt0 + (wave >> 1), qh = wave & 1;
     const int q = qblk * kDqRows + 32 * wave + l32;
     const bool wave_rows = qt_w < nt;
 
     int kt_end = CAUSAL ? min(qt0 + 2, nt) : nt;
     if (VARLEN) kt_end = min(kt_end, ntl);
     if (VARLEN && qt0 >= ntl) kt_end = 0;
+    // Key tiles this wave reads: its dS row's tiles that exist.
+    int kt_end_w = wave_rows && qt_w < ntl ? (CAUSAL ? min(qt_w + 1, kt_end) : kt_end) : 0;
 
     const half_t* Kp = K + ((size_t)b * KV + kv) * (size_t)T * kHeadDim;
-    const half_t* dSh = dS + ((size_t)b * H + h) * (size_t)tiles_per_head * (kTile * kTile);
-    auto tile_valid = [&](int qt, int kt) {
-        return qt < nt && qt < ntl && (!CAUSAL || kt <= qt);
-    };
-    auto tile_ptr = [&](int qt, int kt) {
-        size_t t = CAUSAL ? (size_t)qt * (qt + 1) / 2 + kt : (size_t)qt * nt + kt;
-        return dSh + t * (kTile * kTile);
-    };
+    // This lane's dS words of tile (qt_w, kt): quadrant (qh, kh) at 1024 kh,
+    // key octet kc = 2 (s % 2) + hi at 256 kc, query l32 at 8 l32.
+    const half_t* dSw = dS + ((size_t)b * H + h) * (size_t)tiles_per_head * (kTile * kTile) +
+                        (size_t)(2 * qh) * 1024 + (size_t)hi * 256 + 8 * l32;
+    const size_t row_tiles = CAUSAL ? (size_t)qt_w * (qt_w + 1) / 2 : (size_t)qt_w * nt;
 
-    uint4 reg[6];
-    auto load_tile = [&](int kt) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            int chunk = tid + kDqThreads * u, row = chunk >> 3, col = (chunk & 7) * 8;
-            reg[u] = *(const uint4*)(Kp + (size_t)(kt * kTile + row) * kHeadDim + col);
-        }
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            if (tile_valid(qt0 + r, kt)) {
-                const half_t* tp = tile_ptr(qt0 + r, kt);
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    int chunk = tid + kDqThreads * u;
-                    reg[2 + 2 * r + u] = *(const uint4*)(tp + chunk * 8);
-                }
-            }
-        }
-    };
-    auto store_tile = [&](int kt, int buf) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            int chunk = tid + kDqThreads * u, row = chunk >> 3, col = (chunk & 7) * 8;
-            uint4 v = reg[u];
-            if (VARLEN && kt * kTile + row >= len) v = make_uint4(0, 0, 0, 0);  // padded keys
-            *(uint4*)&lds[buf][0][row * kLdsRow + col] = v;
-        }
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            if (tile_valid(qt0 + r, kt)) {
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    int chunk = tid + kDqThreads * u, row = chunk >> 3, col = (chunk & 7) * 8;
-                    *(uint4*)&lds[buf][1 + r][row * kLdsRow + col] = reg[2 + 2 * r + u];
-                }
-            }
-        }
-    };
+    const int row_a = tid >> 3, row_b = row_a + 32, col8 = (tid & 7) * 8;
+    uint4 ka, kb;
+    half8 bcur[4], bnext[4];
+#define SA_DQ_LOAD_K(kt)                                                                    \
+    do {                                                                                    \
+        const half_t* kt_ = Kp + (size_t)((kt) * kTile) * kHeadDim;                         \
+        ka = *(const uint4*)(kt_ + row_a * kHeadDim + col8);                                \
+        kb = *(const uint4*)(kt_ + row_b * kHeadDim + col8);                                \
+    } while (0)
+#define SA_DQ_STORE_K(kt, buf)                                                              \
+    do {                                                                                    \
+        if (VARLEN && (kt) * kTile + row_a >= len) ka = make_uint4(0, 0, 0, 0);             \
+        if (VARLEN && (kt) * kTile + row_b >= len) kb = make_uint4(0, 0, 0, 0);             \
+        *(uint4*)&lds[buf][row_a * kLdsRow + col8] = ka;                                    \
+        *(uint4*)&lds[buf][row_b * kLdsRow + col8] = kb;                                    \
+    } while (0)
+#define SA_DQ_LOAD_S(kt, dst)                                                               \
+    do {                                                                                    \
+        const half_t* t_ = dSw + (row_tiles + (kt)) * (kTile * kTile);                      \
+        dst[0] = *(const half8*)(t_);                                                       \
+        dst[1] = *(const half8*)(t_ + 512);                                                 \
+        dst[2] = *(const half8*)(t_ + 1024);                                                \
+        dst[3] = *(const half8*)(t_ + 1536);                                                \
+    } while (0)
 
-    f32x16 acc[2] = {zero16(), zero16()};
+    f32x16 acc0 = zero16(), acc1 = zero16();
     if (kt_end > 0) {
-        load_tile(0);
-        store_tile(0, 0);
+        SA_DQ_LOAD_K(0);
+        SA_DQ_STORE_K(0, 0);
     }
+    if (kt_end_w > 0) SA_DQ_LOAD_S(0, bcur);
     __syncthreads();
+    const int trr = (lane & 15) >> 2, trc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     for (int kt = 0; kt < kt_end; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < kt_end) load_tile(kt + 1);
-        if (wave_rows && tile_valid(qt_w, kt)) {
-            const half_t* Ks = lds[buf][0];
-            const half_t* Ss = lds[buf][1 + (wave >> 1)];
-            const int qcol = 32 * (wave & 1);
+        if (kt + 1 < kt_end) SA_DQ_LOAD_K(kt + 1);
+        if (kt + 1 < kt_end_w) SA_DQ_LOAD_S(kt + 1, bnext);
+        if (kt < kt_end_w) {
+            const half_t* Ks = lds[buf];
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4) {
-                half8 bop = cat(lds_read_tr(Ss + tr_offset(lane, 16 * s4, 16 * s4 + 8, qcol)),
-                                lds_read_tr(Ss + tr_offset(lane, 16 * s4 + 4, 16 * s4 + 12, qcol)));
-#pragma unroll
-                for (int db = 0; db < 2; ++db) {
-                    half8 a = cat(lds_read_tr(Ks + tr_offset(lane, 16 * s4, 16 * s4 + 8, 32 * db)),
-                                  lds_read_tr(Ks + tr_offset(lane, 16 * s4 + 4, 16 * s4 + 12, 32 * db)));
-                    acc[db] = mfma32(a, bop, acc[db]);
-                }
+                // A = K^T: lane (d, hi) holds K[16 s4 + 8 hi + 0..7][d].
+                const int r0 = 16 * s4 + 8 * hi + trr;
+                const half8 a0 = cat(lds_read_tr(Ks + r0 * kLdsRow + trc),
+                                     lds_read_tr(Ks + (r0 + 4) * kLdsRow + trc));
+                const half8 a1 = cat(lds_read_tr(Ks + r0 * kLdsRow + 32 + trc),
+                                     lds_read_tr(Ks + (r0 + 4) * kLdsRow + 32 + trc));
+                acc0 = mfma32(a0, bcur[s4], acc0);
+                acc1 = mfma32(a1, bcur[s4], acc1);
             }
         }
-        if (kt + 1 < kt_end) store_tile(kt + 1, buf ^ 1);
+        if (kt + 1 < kt_end) SA_DQ_STORE_K(kt + 1, buf ^ 1);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) bcur[u] = bnext[u];
         __syncthreads();
     }
+#undef SA_DQ_LOAD_K
+#undef SA_DQ_STORE_K
+#undef SA_DQ_LOAD_S
     if (!wave_rows) return;
     float* dq = dQ + (((size_t)b * H + h) * T + q) * kHeadDim;
-    const bool valid = !VARLEN || q < len;
+    const float scale = (!VARLEN || q < len) ? s : 0.0f;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-            f32x4 v = {acc[db][4 * rg], acc[db][4 * rg + 1], acc[db][4 * rg + 2], acc[db][4 * rg + 3]};
-            v *= valid ? s : 0.0f;
-            *(f32x4*)(dq + 32 * db + 8 * rg + 4 * hi) = v;
-        }
+    for (int rg = 0; rg < 4; ++rg) {
+        f32x4 v0 = {acc0[4 * rg], acc0[4 * rg + 1], acc0[4 * rg + 2], acc0[4 * rg + 3]};
+        f32x4 v1 = {acc1[4 * rg], acc1[4 * rg + 1], acc1[4 * rg + 2], acc1[4 * rg + 3]};
+        *(f32x4*)(dq + 8 * rg + 4 * hi) = v0 * scale;
+        *(f32x4*)(dq + 32 + 8 * rg + 4 * hi) = v1 * scale;
+    }
 }
 
 template <bool CAUSAL, bool VARLEN>

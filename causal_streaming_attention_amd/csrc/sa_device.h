@@ -59,6 +59,23 @@ __device__ __forceinline__ float sum_halves(float x) {
 // Round to nearest even binary16.
 __device__ __forceinline__ half_t to_half(float x) { return (half_t)x; }
 
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+// Two floats rounded to nearest even binary16 and packed (v_cvt_pk_f16_f32),
+// the first in the low half.
+__device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
+    half2_t h;
+    h[0] = (half_t)lo;
+    h[1] = (half_t)hi;
+    return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ half8 half8_from_words(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+    uint4 u = make_uint4(w0, w1, w2, w3);
+    return __builtin_bit_cast(half8, u);
+}
+
+// The wave index within the workgroup, as a scalar (wave-uniform) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 typedef __attribute__((address_space(3))) fp16x4_raw lds_fp16x4;
 
 // ds_read_b64_tr_b16 at an LDS element pointer (must point into __shared__ memory).
@@ -66,6 +83,26 @@ __device__ __forceinline__ half4 lds_read_tr(const half_t* p) {
     fp16x4_raw v = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
         (lds_fp16x4*)((__attribute__((address_space(3))) half_t*)(p)));
     return __builtin_bit_cast(half4, v);
+}
+
+// The same transposed read issued as inline assembly: the compiler does not
+// track it, so it adds no wait for unrelated in-flight global-to-LDS loads.
+// The caller must wait with lds_wait() (tying the results) before using them.
+__device__ __forceinline__ half4 lds_read_tr_async(const half_t* p) {
+    half4 r;
+    const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const half_t*)(p);
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+    return r;
+}
+// Wait for every outstanding LDS read of this wave; the operands are tied so
+// no use of them can be scheduled before the wait.
+__device__ __forceinline__ void lds_wait(half4& a, half4& b, half4& c, half4& d, half4& e, half4& f, half4& g,
+                                         half4& h) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h));
+}
+
+__device__ __forceinline__ void lds_wait4(half4& a, half4& b, half4& c, half4& d) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 }
 
 __device__ __forceinline__ half8 cat(const half4& lo, const half4& hi) {
@@ -79,10 +116,10 @@ __device__ __forceinline__ half8 cat(const half4& lo, const half4& hi) {
 // kLdsRow, that a transposed read names so that lane l of a wave receives
 // column (col0 + 16 * ((l / 16) % 2) + l % 16) at rows row0(l) + 0..3, where
 // row0 = rowA for lanes 0..31 and rowB for lanes 32..63.
-__device__ __forceinline__ int tr_offset(int lane, int rowA, int rowB, int col0) {
+__device__ __forceinline__ int tr_offset(int lane, int rowA, int rowB, int col0, int stride = kLdsRow) {
     int row0 = (lane & 32) ? rowB : rowA;
     int r = (lane & 15) >> 2, chunk = lane & 3;
-    return (row0 + r) * kLdsRow + col0 + 16 * ((lane >> 4) & 1) + 4 * chunk;
+    return (row0 + r) * stride + col0 + 16 * ((lane >> 4) & 1) + 4 * chunk;
 }
 
 }  // namespace sa
