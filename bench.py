@@ -111,6 +111,83 @@ def _cpu_model():
     return "unknown"
 
 
+KERNEL_NAMES = {"forward": "sa_forward_kernel", "row_terms": "sa_row_terms_kernel", "key_pass": "sa_key_kernel",
+                "dq_pass": "sa_dq_kernel"}
+
+
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(dirpath, suffix):
+    for root, _, files in os.walk(dirpath):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    raise FileNotFoundError(f"no *{suffix} under {dirpath}")
+
+
+def summarize_profile(dirs, workload, command):
+    """Write profiles/kernel_trace_<workload>.txt from a --kernel-trace --stats run and, given the
+    FETCH_SIZE and WRITE_SIZE pass directories of a --calibrate-copy-mb run, profiles/traffic.json
+    and profiles/hbm_traffic_<workload>.txt.  Counter bytes are scaled by what the same counter
+    reads for the closing device copy, whose bytes are known."""
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    trace_dir = dirs[0]
+    stats = _read_csv(_find(trace_dir, "kernel_stats.csv"))
+    lines = [f"# rocprofv3 kernel trace, workload {workload}", f"# command: {command}", "",
+             f"{'kernel':<12} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}"]
+    for short, key in KERNEL_NAMES.items():
+        for r in stats:
+            if key in r["Name"]:
+                lines.append(f"{short:<12} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
+                             f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f}")
+    with open(os.path.join(ROOT, "profiles", f"kernel_trace_{workload}.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    if len(dirs) < 3:
+        return
+    per = {}
+    for label, d in (("FETCH_SIZE", dirs[1]), ("WRITE_SIZE", dirs[2])):
+        rows = [r for r in _read_csv(_find(d, "counter_collection.csv")) if r["Counter_Name"] == label]
+        last = max(rows, key=lambda r: int(r["Dispatch_Id"]))          # the calibration copy
+        copy_kib = float(last["Counter_Value"])
+        per[label] = {"copy_kib": copy_kib, "kernels": {}}
+        for short, key in KERNEL_NAMES.items():
+            vals = [float(r["Counter_Value"]) for r in rows if key in r["Kernel_Name"]]
+            if vals:
+                per[label]["kernels"][short] = sum(vals) / len(vals)
+    import re
+    m = re.search(r"--calibrate-copy-mb[= ](\d+)", command)
+    copy_bytes = int(m.group(1)) << 20 if m else None
+    if copy_bytes is None:
+        raise ValueError("--profile-command must name --calibrate-copy-mb=N")
+    fr = copy_bytes / (per["FETCH_SIZE"]["copy_kib"] * 1024)
+    fw = copy_bytes / (per["WRITE_SIZE"]["copy_kib"] * 1024)
+    traffic = {"workload": workload, "source_hash": kernel_source_hash(), "command": command,
+               "copy_bytes": copy_bytes, "fetch_scale": fr, "write_scale": fw, "kernels": {}}
+    lines = [f"# rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE (KiB per dispatch), workload {workload}",
+             f"# command: {command}",
+             f"# scale: a {copy_bytes >> 20} MiB device copy reads FETCH_SIZE {per['FETCH_SIZE']['copy_kib']:.0f} KiB "
+             f"and WRITE_SIZE {per['WRITE_SIZE']['copy_kib']:.0f} KiB: read x{fr:.3f}, write x{fw:.3f}", "",
+             f"{'kernel':<12} {'FETCH_KiB':>12} {'WRITE_KiB':>12} {'read_MB':>10} {'write_MB':>10}"]
+    for short in KERNEL_NAMES:
+        fk = per["FETCH_SIZE"]["kernels"].get(short)
+        wk = per["WRITE_SIZE"]["kernels"].get(short)
+        if fk is None or wk is None:
+            continue
+        rb, wb = fk * 1024 * fr, wk * 1024 * fw
+        traffic["kernels"][short] = {"read_bytes": rb, "write_bytes": wb, "hbm_bytes_per_launch": rb + wb}
+        lines.append(f"{short:<12} {fk:>12.0f} {wk:>12.0f} {rb / 1e6:>10.1f} {wb / 1e6:>10.1f}")
+    with open(os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(traffic, f, indent=1)
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,7 +196,17 @@ def main():
     ap.add_argument("--workload", default="causal_gqa_t4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--block-order", type=int, default=0)
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="after the timed steps, run one device copy of this many MiB (the reference dispatch "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--summarize-profile", nargs="+", metavar="DIR",
+                    help="summarize rocprofv3 output directories (kernel trace, then FETCH_SIZE and WRITE_SIZE "
+                         "passes of a --calibrate-copy-mb run) into profiles/ and exit")
+    ap.add_argument("--profile-command", default="", help="command line recorded in the summaries")
     args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile, args.workload, args.profile_command)
+        return
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
               "(the sharding plan is design only)", file=sys.stderr)
@@ -185,6 +272,14 @@ def main():
             e["gb_per_s"] = round(gbs, 1)
             e["frac_hbm_peak"] = round(gbs / HBM_PEAK_GBS, 4)
         kernels[n] = e
+
+    if args.calibrate_copy_mb > 0:
+        n = args.calibrate_copy_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)      # the last dispatch of the run: n bytes read, n bytes written
+        torch.cuda.synchronize()
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

@@ -79,9 +79,9 @@ __global__ __launch_bounds__(kRowThreads) void sa_row_terms_kernel(const half_t*
 // The slots' dK and dV are then summed through LDS in slot order, dK scaled
 // by s, and stored with coalesced 16-byte writes.
 //
-// A staged 32 x 64 fp16 sub-tile has 128-byte rows whose 16-byte chunk c of
-// row r sits at chunk c ^ (r % 8): the eight rows a 16-lane read touches fall
-// in distinct banks without padding (which direct loads cannot make).
+// A staged 32 x 64 fp16 sub-tile has 128-byte rows whose 16-byte chunks are
+// permuted per row (swz below) so that its reads meet no bank conflict
+// without padding (which direct loads cannot make).
 // ---------------------------------------------------------------------------
 constexpr int kSubRows = 32;
 constexpr int kSubBytes = kSubRows * kHeadDim * 2;          // 4096
@@ -99,9 +99,14 @@ struct KeyLds {
     static constexpr int bytes = stage > red ? (stage > vt ? stage : vt) : (red > vt ? red : vt);
 };
 
+// The chunk permutation of a staged sub-tile's row: f(r) is distinct for any 8
+// consecutive rows (a 16-byte read by 8 lanes of 8 rows) and f(r) / 2 is
+// distinct within each aligned group of 4 rows (a transposed read of 4 rows x
+// 2 chunks), so neither read pattern meets a bank conflict.
+__device__ __forceinline__ int swz_key(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 // Element offset of (row, col) in a swizzled 32 x 64 sub-tile.
 __device__ __forceinline__ int swz(int row, int col) {
-    return row * kHeadDim + ((((col >> 3) ^ row) & 7) << 3) + (col & 7);
+    return row * kHeadDim + (((col >> 3) ^ swz_key(row)) << 3) + (col & 7);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -182,19 +187,16 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     char* const wstage = smem + wave * kWaveBytes;  // this wave's two item buffers
     half_t* const dsx = (half_t*)(wstage + 2 * kItemBytes);  // and its dS block [key][query]
     const int dma_row = lane >> 3;                         // + 8 u
-    auto item_head = [&](int it) { return kv * G + (it / n_sub) * GW + slot; };
-    auto item_sub = [&](int it) { return sub_hi - 1 - (it % n_sub); };
     // Direct loads of one item into buffer `buf`: 4 x 1 KB of Q rows, 4 x 1 KB
     // of dO rows (lane l of load u: row 8 u + l / 8, stored chunk l % 8 holding
-    // the row's chunk (l % 8) ^ (row % 8)), then L (lanes 0..31) and D (32..63).
-    auto issue_item = [&](int it, int buf) {
-        const int head = item_head(it), sub = item_sub(it);
+    // the row's chunk (l % 8) ^ swz_key(row)), then L (lanes 0..31) and D (32..63).
+    auto issue_item = [&](int head, int sub, int buf) {
         const size_t rowbase = ((size_t)b * H + head) * T + (size_t)sub * kSubRows;
         char* base = wstage + buf * kItemBytes;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int row = 8 * u + dma_row;
-            const int col = (((lane & 7) ^ row) & 7) * 8;
+            const int col = ((lane & 7) ^ swz_key(row)) * 8;
             const size_t off = (rowbase + row) * kHeadDim + col;
             dma16(Q + off, base + 1024 * u);
             dma16(dO + off, base + kSubBytes + 1024 * u);
@@ -203,12 +205,18 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
         dma4(src, base + 2 * kSubBytes);
     };
 
-    if (n_items > 0) issue_item(0, 0);
+    // Items in order: for each of the slot's heads, sub-tiles from the last down.
+    int head = kv * G + slot, sub = sub_hi - 1;
+    if (n_items > 0) issue_item(head, sub, 0);
 
     for (int it = 0; it < n_items; ++it) {
         const int buf = it & 1;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this item has landed in LDS
-        const int head = item_head(it), sub = item_sub(it);
+        int next_head = head, next_sub = sub - 1;
+        if (next_sub < sub_lo) {
+            next_sub = sub_hi - 1;
+            next_head += GW;
+        }
         const int qb = sub * kSubRows;
         half_t* Qs = (half_t*)(wstage + buf * kItemBytes);
         half_t* dOs = Qs + kSubRows * kHeadDim;
@@ -227,7 +235,7 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
             }
             if ((lane & 31) >= keep) Ls[lane] = 0.0f;  // L (lanes 0..31) and D (32..63)
         }
-        if (it + 1 < n_items) issue_item(it + 1, buf ^ 1);
+        if (it + 1 < n_items) issue_item(next_head, next_sub, buf ^ 1);
 
         // This wave's 32x32 block of the 64x64 dS tile: quadrant (query half
         // sub % 2, key half khalf), stored as [key octet 4][query 32][8 keys].
@@ -236,13 +244,9 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
         half_t* dsp = dS + (((size_t)b * H + head) * (size_t)tiles_per_head + tile) * (kTile * kTile) +
                       (size_t)(2 * (sub & 1) + khalf) * 1024 + 8 * lane;
 
-        const bool all_masked = (CAUSAL && qb + kSubRows - 1 < kbase) ||
-                                (VARLEN && (qb >= len || kbase >= len));
-        if (all_masked) {
-            *(uint4*)dsp = make_uint4(0, 0, 0, 0);
-            *(uint4*)(dsp + 512) = make_uint4(0, 0, 0, 0);
-            continue;
-        }
+        // A block with no admitted pair (the diagonal sub-tile of the upper key
+        // half, padding) goes through the same code: the mask makes its P and
+        // dS exact zeros.
         f32x16 sacc = zero16(), pacc = zero16();
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
@@ -323,6 +327,8 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
         dvacc1 = mfma32(cat(t[10], t[11]), pp1, dvacc1);
         dkacc0 = mfma32(cat(t[12], t[13]), pd1, dkacc0);
         dkacc1 = mfma32(cat(t[14], t[15]), pd1, dkacc1);
+        head = next_head;
+        sub = next_sub;
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // every wave is done with its staging buffers
@@ -371,18 +377,20 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
 // dQ pass.  One 256-thread workgroup per 128 queries of a query head (two dS
 // tile rows); wave w owns 32 queries.  For each key tile up to the diagonal
 // (the query pass's order) the K tile is staged in LDS for the four waves
-// (double-buffered) and each wave accumulates
+// (double-buffered, its global loads two tiles ahead) and each wave
+// accumulates
 //   dQ^T += K^T dS^T   (A = K^T by transposed LDS reads; B = dS^T straight
 //                       from the workspace: its quadrant layout puts the 8
 //                       keys a lane needs for one query in 16 contiguous
 //                       bytes, and a wave's loads in two 512-byte runs)
-// with the next tile's dS loads in flight; each lane ends with 4-float runs of
-// one query's dQ row: dQ = s * sum, stored with 16-byte writes.
+// with the dS loads of the next three tiles in flight, since the pass streams
+// the workspace from memory.  Each lane ends with 4-float runs of one query's
+// dQ row: dQ = s * sum, stored with 16-byte writes.
 // ---------------------------------------------------------------------------
 constexpr int kDqWaves = 4;
 constexpr int kDqRows = 32 * kDqWaves;
 constexpr int kDqThreads = 64 * kDqWaves;
-constexpr int kTileHalvesDq = kTile * kLdsRow;
+constexpr int kKTileHalves = kTile * kHeadDim;  // unpadded, chunk-swizzled
 
 template <bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __restrict__ K,
@@ -391,7 +399,7 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
                                                                const int32_t* __restrict__ seqlens, float s,
                                                                int T, int H, int KV, int n_qblk, int BH,
                                                                int block_order, long long tiles_per_head) {
-    __shared__ __attribute__((aligned(16))) half_t lds[2][kTileHalvesDq];  // K tiles
+    __shared__ __attribute__((aligned(16))) half_t lds[2][kKTileHalves];  // K tiles
 
     const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -416,74 +424,85 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
     if (VARLEN) kt_end = min(kt_end, ntl);
     if (VARLEN && qt0 >= ntl) kt_end = 0;
     // Key tiles this wave reads: its dS row's tiles that exist.
-    int kt_end_w = wave_rows && qt_w < ntl ? (CAUSAL ? min(qt_w + 1, kt_end) : kt_end) : 0;
+    const int kt_end_w = wave_rows && qt_w < ntl ? (CAUSAL ? min(qt_w + 1, kt_end) : kt_end) : 0;
 
     const half_t* Kp = K + ((size_t)b * KV + kv) * (size_t)T * kHeadDim;
     // This lane's dS words of tile (qt_w, kt): quadrant (qh, kh) at 1024 kh,
     // key octet kc = 2 (s % 2) + hi at 256 kc, query l32 at 8 l32.
     const half_t* dSw = dS + ((size_t)b * H + h) * (size_t)tiles_per_head * (kTile * kTile) +
-                        (size_t)(2 * qh) * 1024 + (size_t)hi * 256 + 8 * l32;
-    const size_t row_tiles = CAUSAL ? (size_t)qt_w * (qt_w + 1) / 2 : (size_t)qt_w * nt;
+                        (size_t)(2 * qh) * 1024 + (size_t)hi * 256 + 8 * l32 +
+                        (CAUSAL ? (size_t)qt_w * (qt_w + 1) / 2 : (size_t)qt_w * nt) * (kTile * kTile);
 
-    const int row_a = tid >> 3, row_b = row_a + 32, col8 = (tid & 7) * 8;
-    uint4 ka, kb;
-    half8 bcur[4], bnext[4];
-#define SA_DQ_LOAD_K(kt)                                                                    \
-    do {                                                                                    \
-        const half_t* kt_ = Kp + (size_t)((kt) * kTile) * kHeadDim;                         \
-        ka = *(const uint4*)(kt_ + row_a * kHeadDim + col8);                                \
-        kb = *(const uint4*)(kt_ + row_b * kHeadDim + col8);                                \
-    } while (0)
-#define SA_DQ_STORE_K(kt, buf)                                                              \
-    do {                                                                                    \
-        if (VARLEN && (kt) * kTile + row_a >= len) ka = make_uint4(0, 0, 0, 0);             \
-        if (VARLEN && (kt) * kTile + row_b >= len) kb = make_uint4(0, 0, 0, 0);             \
-        *(uint4*)&lds[buf][row_a * kLdsRow + col8] = ka;                                    \
-        *(uint4*)&lds[buf][row_b * kLdsRow + col8] = kb;                                    \
-    } while (0)
-#define SA_DQ_LOAD_S(kt, dst)                                                               \
-    do {                                                                                    \
-        const half_t* t_ = dSw + (row_tiles + (kt)) * (kTile * kTile);                      \
-        dst[0] = *(const half8*)(t_);                                                       \
-        dst[1] = *(const half8*)(t_ + 512);                                                 \
-        dst[2] = *(const half8*)(t_ + 1024);                                                \
-        dst[3] = *(const half8*)(t_ + 1536);                                                \
-    } while (0)
+    // K staging: thread tid moves 16-byte chunks (row_a, c) and (row_a + 32, c),
+    // stored at chunk c ^ swz_key(row) of the row.
+    const int row_a = tid >> 3, row_b = row_a + 32, chk = tid & 7;
+    const int st_a = row_a * kHeadDim + ((chk ^ swz_key(row_a)) << 3);
+    const int st_b = row_b * kHeadDim + ((chk ^ swz_key(row_b)) << 3);
+    uint4 k1a, k1b, k2a, k2b;  // K tiles kt + 1 and kt + 2 in flight
+    auto load_k = [&](int kt, uint4& ra, uint4& rb) {
+        const half_t* kt_ = Kp + (size_t)(kt * kTile) * kHeadDim + chk * 8;
+        ra = *(const uint4*)(kt_ + row_a * kHeadDim);
+        rb = *(const uint4*)(kt_ + row_b * kHeadDim);
+    };
+    auto store_k = [&](int kt, int buf, uint4 ra, uint4 rb) {
+        if (VARLEN && kt * kTile + row_a >= len) ra = make_uint4(0, 0, 0, 0);  // padded keys
+        if (VARLEN && kt * kTile + row_b >= len) rb = make_uint4(0, 0, 0, 0);
+        *(uint4*)&lds[buf][st_a] = ra;
+        *(uint4*)&lds[buf][st_b] = rb;
+    };
+    half8 b0[4], b1[4], b2[4], b3[4];  // dS operands of tiles kt .. kt + 3
+    auto load_s = [&](int kt, half8* dst) {
+        const half_t* t_ = dSw + (size_t)kt * (kTile * kTile);
+        dst[0] = *(const half8*)(t_);
+        dst[1] = *(const half8*)(t_ + 512);
+        dst[2] = *(const half8*)(t_ + 1024);
+        dst[3] = *(const half8*)(t_ + 1536);
+    };
 
     f32x16 acc0 = zero16(), acc1 = zero16();
     if (kt_end > 0) {
-        SA_DQ_LOAD_K(0);
-        SA_DQ_STORE_K(0, 0);
+        uint4 ra, rb;
+        load_k(0, ra, rb);
+        store_k(0, 0, ra, rb);
+        if (kt_end > 1) load_k(1, k1a, k1b);
     }
-    if (kt_end_w > 0) SA_DQ_LOAD_S(0, bcur);
+    if (kt_end_w > 0) load_s(0, b0);
+    if (kt_end_w > 1) load_s(1, b1);
+    if (kt_end_w > 2) load_s(2, b2);
     __syncthreads();
     const int trr = (lane & 15) >> 2, trc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     for (int kt = 0; kt < kt_end; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < kt_end) SA_DQ_LOAD_K(kt + 1);
-        if (kt + 1 < kt_end_w) SA_DQ_LOAD_S(kt + 1, bnext);
+        if (kt + 2 < kt_end) load_k(kt + 2, k2a, k2b);
+        if (kt + 3 < kt_end_w) load_s(kt + 3, b3);
         if (kt < kt_end_w) {
             const half_t* Ks = lds[buf];
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4) {
                 // A = K^T: lane (d, hi) holds K[16 s4 + 8 hi + 0..7][d].
                 const int r0 = 16 * s4 + 8 * hi + trr;
-                const half8 a0 = cat(lds_read_tr(Ks + r0 * kLdsRow + trc),
-                                     lds_read_tr(Ks + (r0 + 4) * kLdsRow + trc));
-                const half8 a1 = cat(lds_read_tr(Ks + r0 * kLdsRow + 32 + trc),
-                                     lds_read_tr(Ks + (r0 + 4) * kLdsRow + 32 + trc));
-                acc0 = mfma32(a0, bcur[s4], acc0);
-                acc1 = mfma32(a1, bcur[s4], acc1);
+                const half8 a0 = cat(lds_read_tr(Ks + r0 * kHeadDim + (((trc >> 3) ^ swz_key(r0)) << 3) + (trc & 7)),
+                                     lds_read_tr(Ks + (r0 + 4) * kHeadDim +
+                                                 (((trc >> 3) ^ swz_key(r0 + 4)) << 3) + (trc & 7)));
+                const half8 a1 = cat(lds_read_tr(Ks + r0 * kHeadDim +
+                                                 ((((trc + 32) >> 3) ^ swz_key(r0)) << 3) + (trc & 7)),
+                                     lds_read_tr(Ks + (r0 + 4) * kHeadDim +
+                                                 ((((trc + 32) >> 3) ^ swz_key(r0 + 4)) << 3) + (trc & 7)));
+                acc0 = mfma32(a0, b0[s4], acc0);
+                acc1 = mfma32(a1, b0[s4], acc1);
             }
         }
-        if (kt + 1 < kt_end) SA_DQ_STORE_K(kt + 1, buf ^ 1);
+        if (kt + 1 < kt_end) store_k(kt + 1, buf ^ 1, k1a, k1b);
+        k1a = k2a;
+        k1b = k2b;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) bcur[u] = bnext[u];
+        for (int u = 0; u < 4; ++u) {
+            b0[u] = b1[u];
+            b1[u] = b2[u];
+            b2[u] = b3[u];
+        }
         __syncthreads();
     }
-#undef SA_DQ_LOAD_K
-#undef SA_DQ_STORE_K
-#undef SA_DQ_LOAD_S
     if (!wave_rows) return;
     float* dq = dQ + (((size_t)b * H + h) * T + q) * kHeadDim;
     const float scale = (!VARLEN || q < len) ? s : 0.0f;
