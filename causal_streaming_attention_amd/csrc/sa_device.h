@@ -56,6 +56,35 @@ __device__ __forceinline__ float sum_halves(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// s_waitcnt vmcnt(0) as a compiler-visible wait (expcnt and lgkmcnt left at
+// their maxima): the wait-insertion pass folds it into its own count, so
+// loads that are known to have landed stop being treated as outstanding.
+__device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Block schedule shared by the kernels whose per-tile work follows the causal
+// triangle.  Tile t and tile n - 1 - t form a pair whose two walks add up to
+// the same length for every t, so a grid of (pairs x units) blocks, each doing
+// its pair's two tiles, is balanced with no tail of short blocks.  A unit is a
+// (batch, head) or a (batch, kv head); units come in groups that read the same
+// K/V (the query heads of one kv head).  The chip hands workgroups to its 8
+// XCDs round-robin by index, each XCD with its own L2: when the group count is
+// a multiple of 8, XCD x is given whole groups (x, x + 8, ...), so a group's
+// K/V is cached in one L2 instead of in all eight.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void pair_schedule(int block, int n_groups, int group_size, int& pair, int& unit) {
+    const int n_units = n_groups * group_size;
+    if (n_groups % kXcds == 0) {
+        const int xcd = block % kXcds, k = block / kXcds;
+        const int units_per_xcd = (n_groups / kXcds) * group_size;
+        pair = k / units_per_xcd;
+        const int r = k % units_per_xcd;
+        unit = ((r / group_size) * kXcds + xcd) * group_size + r % group_size;
+    } else {
+        pair = block / n_units;
+        unit = block % n_units;
+    }
+}
+
 // Round to nearest even binary16.
 __device__ __forceinline__ half_t to_half(float x) { return (half_t)x; }
 

@@ -11,16 +11,25 @@
 // MI355X design (not the pages' SM86 one): a 256-thread workgroup (4 wave64s)
 // takes 128 queries of one query head; each wave owns 32 queries.  Each key
 // tile's K rows and V^T rows are staged once in LDS for all four waves with
-// coalesced 16-byte loads, double-buffered, the next tile's global loads in
-// flight while the current tile computes.  A wave computes S^T = K Q^T with
-// v_mfma_f32_32x32x16_f16 (A = K rows from LDS, B = the wave's Q kept in
-// registers), so every lane holds 32 scores of ONE query: the row maximum is
-// an in-lane max plus one v_permlane32_swap, the row sum stays a per-lane
-// partial until the end (as the pages keep it per thread), and the rescale
-// factor is per lane.  The fp16 P^T accumulators feed O^T += V^T P^T directly
-// as the B operand: the contraction order over the tile's keys is permuted to
-// match the accumulator layout, and V^T's A operand is read from LDS in the
-// same permuted order, so P never leaves registers.
+// coalesced 16-byte loads (K two tiles ahead, V^T one tile ahead).  A wave
+// computes S^T = K Q^T with v_mfma_f32_32x32x16_f16 (A = K rows from LDS,
+// B = the wave's Q kept in registers), so every lane holds 32 scores of ONE
+// query: the row maximum is an in-lane max plus one v_permlane32_swap, the
+// row sum stays a per-lane partial until the end (as the pages keep it per
+// thread), and the rescale factor is per lane.  The fp16 P^T accumulators
+// feed O^T += V^T P^T directly as the B operand: the contraction order over
+// the tile's keys is permuted to match the accumulator layout, and V^T's A
+// operand is read from LDS in the same permuted order, so P never leaves
+// registers.
+//
+// The loop is software-pipelined: while tile j's softmax runs on the vector
+// unit, the wave's matrix-core work is tile j + 1's scores and tile j - 1's
+// P V, issued between the softmax instructions.  The maximum used for the
+// exponents moves only when some row of the wave exceeds it by more than 8
+// (base 2), so P <= 2^8 and the O/l rescale is rare; O / l and L = m + log2 l
+// are the same quantities whichever maximum the exponents used.  Blocks take
+// the query tiles (n - 1 - p, p) in pairs of equal causal length, with the
+// heads that share a kv head kept on one XCD (pair_schedule).
 #include "sa_device.h"
 #include "sa_internal.h"
 
@@ -31,7 +40,14 @@ namespace {
 constexpr int kFwdWaves = 4;
 constexpr int kFwdRows = 32 * kFwdWaves;     // queries per workgroup
 constexpr int kFwdThreads = 64 * kFwdWaves;
-constexpr int kTileHalves = kTile * kLdsRow; // one padded 64-row tile in LDS
+constexpr int kTileHalves = kTile * kLdsRow; // one padded 64-row K tile in LDS
+// V^T rows are padded to 68 halves (34 dwords): sixteen lanes reading 8 bytes
+// from sixteen consecutive rows then touch 32 distinct banks.
+constexpr int kVRow = 68;
+constexpr int kVTileHalves = kTile * kVRow;
+// The running maximum used for the exponents moves only when some row of the
+// wave sees a scaled score more than this far (base 2) above it, so P <= 2^8.
+constexpr float kMaxSlack = 8.0f;
 
 // Zero the halves of an 8-half chunk at positions >= keep (keep may be <= 0 or >= 8).
 __device__ __forceinline__ uint4 clear_tail(uint4 v, int keep) {
@@ -42,28 +58,54 @@ __device__ __forceinline__ uint4 clear_tail(uint4 v, int keep) {
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Issue-order hints for one tile of the loop: the 16 products (8 for the next
+// tile's scores, 8 for the previous tile's P V) spread through the softmax's
+// vector work, with the LDS operand reads ahead of them.
+#define SA_SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+#define SA_FWD_SLOT_R SA_SGB(0x008, 1); SA_SGB(0x002, 6); SA_SGB(0x100, 1)
+#define SA_FWD_SLOT SA_SGB(0x008, 1); SA_SGB(0x002, 6)
+#define SA_FWD_INTERLEAVE()                                       \
+    do {                                                          \
+        SA_SGB(0x100, 8);                                         \
+        SA_FWD_SLOT_R; SA_FWD_SLOT_R; SA_FWD_SLOT_R; SA_FWD_SLOT_R; \
+        SA_FWD_SLOT_R; SA_FWD_SLOT_R; SA_FWD_SLOT_R; SA_FWD_SLOT_R; \
+        SA_FWD_SLOT; SA_FWD_SLOT; SA_FWD_SLOT; SA_FWD_SLOT;       \
+        SA_FWD_SLOT; SA_FWD_SLOT; SA_FWD_SLOT; SA_FWD_SLOT;       \
+    } while (0)
+
 template <bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
     const half_t* __restrict__ Q, const half_t* __restrict__ K, const half_t* __restrict__ Vt,
     half_t* __restrict__ O, float* __restrict__ L, const int32_t* __restrict__ seqlens, float c, int T,
     int H, int KV, int n_qtiles, int BH, int block_order) {
-    __shared__ __attribute__((aligned(16))) half_t lds[2][2][kTileHalves];  // [buffer][K | V^T][row][col]
+    // K tile j + 2 is staged while tile j + 1's scores are formed, and V^T
+    // tile j + 1 while tile j - 1's products are summed: two K buffers and
+    // three V^T buffers (V^T tile j lives in buffer j % 3).
+    __shared__ __attribute__((aligned(16))) half_t kls[2][kTileHalves];
+    __shared__ __attribute__((aligned(16))) half_t vls[3][kVTileHalves];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int l32 = lane & 31, hi = lane >> 5;
 
-    // Block -> (query tile, batch*head).  Order 0 walks the query tiles from
-    // the last (longest causal walk) down, one tile of every head at a time.
-    int qtile, bh;
+    // Block -> (batch*head, query tiles).  Order 0: the pair of query tiles
+    // (n - 1 - p, p), whose causal walks add up to the same length for every
+    // p, with the heads of one kv head kept on one XCD.  Order 1: one query
+    // tile per block in plain order.
+    int bh, n_items, items[2];
     if (block_order == 0) {
-        qtile = n_qtiles - 1 - (int)(blockIdx.x / BH);
-        bh = (int)(blockIdx.x % BH);
+        int pair;
+        pair_schedule((int)blockIdx.x, (BH / H) * KV, H / KV, pair, bh);
+        items[0] = n_qtiles - 1 - pair;
+        items[1] = pair;
+        n_items = pair < items[0] ? 2 : 1;
     } else {
-        qtile = (int)(blockIdx.x % n_qtiles);
+        items[0] = items[1] = (int)(blockIdx.x % n_qtiles);
         bh = (int)(blockIdx.x / n_qtiles);
+        n_items = 1;
     }
     const int b = bh / H, h = bh % H, kv = h / (H / KV);
     const int len = VARLEN ? min(max(seqlens[b], 0), T) : T;
+    auto process = [&](const int qtile) {
     const int q0 = qtile * kFwdRows;
     const int qw = q0 + 32 * wave;                 // this wave's first query (scalar)
     const int q = qw + l32;                        // this lane's query
@@ -77,6 +119,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
     int kend_w = CAUSAL ? qw + 32 : T;
     if (VARLEN) kend_w = min(kend_w, len);
     const bool wave_live = wave_rows && qw < row_limit;
+    const int n_kt_w = wave_live ? min((kend_w + kTile - 1) / kTile, n_kt) : 0;  // tiles this wave uses
 
     const size_t kv_off = ((size_t)b * KV + kv) * (size_t)T * kHeadDim;
     const half_t* Kp = K + kv_off;
@@ -93,54 +136,91 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
 
     f32x16 oacc0 = zero16(), oacc1 = zero16();  // O^T, d blocks 0..31 and 32..63
     float m = kNegInf, lsum = 0.0f;
+    // O's move to a new maximum is applied one step late, just before the
+    // next tile's products are added: the step that raises the maximum still
+    // has the previous tile's products in flight.
+    bool rescale = false;
+    float alpha = 1.0f;
+    auto apply_rescale = [&]() {
+        if (rescale) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                oacc0[r] *= alpha;
+                oacc1[r] *= alpha;
+            }
+        }
+    };
 
     // Staging: 512 16-byte chunks per 64x64 tile; thread tid moves chunks
-    // tid and tid + 256 of K and of V^T.
+    // (row_a, col8) and (row_a + 32, col8) of a K tile and of a V^T tile.
     const int row_a = tid >> 3, row_b = row_a + 32, col8 = (tid & 7) * 8;
-    uint4 ka, kb, va, vb;
-#define SA_FWD_LOAD(j)                                                                      \
-    do {                                                                                    \
-        const half_t* kt_ = Kp + (size_t)((j) * kTile) * kHeadDim;                          \
-        ka = *(const uint4*)(kt_ + row_a * kHeadDim + col8);                                \
-        kb = *(const uint4*)(kt_ + row_b * kHeadDim + col8);                                \
-        va = *(const uint4*)(Vp + (size_t)row_a * T + (j) * kTile + col8);                  \
-        vb = *(const uint4*)(Vp + (size_t)row_b * T + (j) * kTile + col8);                  \
-    } while (0)
-#define SA_FWD_STORE(j, buf)                                                                \
-    do {                                                                                    \
-        if (VARLEN && (j) * kTile + col8 + 8 > len) {                                       \
-            /* keys at or past the length carry P = 0: clear their V entries */             \
-            va = clear_tail(va, len - ((j) * kTile + col8));                                \
-            vb = clear_tail(vb, len - ((j) * kTile + col8));                                \
-        }                                                                                   \
-        *(uint4*)&lds[buf][0][row_a * kLdsRow + col8] = ka;                                 \
-        *(uint4*)&lds[buf][0][row_b * kLdsRow + col8] = kb;                                 \
-        *(uint4*)&lds[buf][1][row_a * kLdsRow + col8] = va;                                 \
-        *(uint4*)&lds[buf][1][row_b * kLdsRow + col8] = vb;                                 \
-    } while (0)
-
-    if (n_kt > 0) {
-        SA_FWD_LOAD(0);
-        SA_FWD_STORE(0, 0);
-    }
-    __syncthreads();
-
-    for (int j = 0; j < n_kt; ++j) {
-        const int buf = j & 1;
-        if (j + 1 < n_kt) SA_FWD_LOAD(j + 1);
-
-        if (wave_live && j * kTile < kend_w) {
-            const half_t* Ks = lds[buf][0];
-            const half_t* Vs = lds[buf][1];
-            // S^T = K Q^T for the tile's two 32-key blocks.
-            f32x16 s0 = zero16(), s1 = zero16();
+    auto load_k = [&](int j, uint4& ra, uint4& rb) {
+        const half_t* kt_ = Kp + (size_t)(j * kTile) * kHeadDim + col8;
+        ra = *(const uint4*)(kt_ + row_a * kHeadDim);
+        rb = *(const uint4*)(kt_ + row_b * kHeadDim);
+    };
+    auto load_v = [&](int j, uint4& ra, uint4& rb) {
+        ra = *(const uint4*)(Vp + (size_t)row_a * T + j * kTile + col8);
+        rb = *(const uint4*)(Vp + (size_t)row_b * T + j * kTile + col8);
+    };
+    auto store_k = [&](int buf, const uint4& ra, const uint4& rb) {
+        *(uint4*)&kls[buf][row_a * kLdsRow + col8] = ra;
+        *(uint4*)&kls[buf][row_b * kLdsRow + col8] = rb;
+    };
+    auto store_v = [&](int j, int buf, uint4 ra, uint4 rb) {
+        if (VARLEN && j * kTile + col8 + 8 > len) {
+            // keys at or past the length carry P = 0: clear their V entries
+            ra = clear_tail(ra, len - (j * kTile + col8));
+            rb = clear_tail(rb, len - (j * kTile + col8));
+        }
+        // 68-half rows are 8-byte aligned: two 8-byte stores per chunk
+        half_t* da = &vls[buf][row_a * kVRow + col8];
+        half_t* db = &vls[buf][row_b * kVRow + col8];
+        *(uint2*)da = make_uint2(ra.x, ra.y);
+        *(uint2*)(da + 4) = make_uint2(ra.z, ra.w);
+        *(uint2*)db = make_uint2(rb.x, rb.y);
+        *(uint2*)(db + 4) = make_uint2(rb.z, rb.w);
+    };
+    // S^T = K Q^T for a tile's two 32-key blocks.
+    auto scores = [&](const half_t* Ks, f32x16& s0, f32x16& s1) {
+        s0 = zero16();
+        s1 = zero16();
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                half8 a0 = *(const half8*)(Ks + l32 * kLdsRow + 16 * s + 8 * hi);
-                half8 a1 = *(const half8*)(Ks + (32 + l32) * kLdsRow + 16 * s + 8 * hi);
-                s0 = mfma32(a0, qf[s], s0);
-                s1 = mfma32(a1, qf[s], s1);
-            }
+        for (int s = 0; s < 4; ++s) {
+            const half8 a0 = *(const half8*)(Ks + l32 * kLdsRow + 16 * s + 8 * hi);
+            const half8 a1 = *(const half8*)(Ks + (32 + l32) * kLdsRow + 16 * s + 8 * hi);
+            s0 = mfma32(a0, qf[s], s0);
+            s1 = mfma32(a1, qf[s], s1);
+        }
+    };
+    // O^T += V^T P^T for one tile, P^T given as the 16 packed words of the
+    // four 16-key k-steps.  k-step s covers the tile's keys 16 s + 4 hi + 0..3
+    // and 16 s + 8 + 4 hi + 0..3 (the score accumulator's order), and V^T's A
+    // operand is read in that same order.
+    auto pv = [&](const half_t* Vs, const uint32_t (&w)[16]) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const half8 pb = half8_from_words(w[4 * s], w[4 * s + 1], w[4 * s + 2], w[4 * s + 3]);
+            const half_t* v0 = Vs + l32 * kVRow + 16 * s + 4 * hi;
+            const half_t* v1 = v0 + 32 * kVRow;
+            oacc0 = mfma32(cat(*(const half4*)v0, *(const half4*)(v0 + 8)), pb, oacc0);
+            oacc1 = mfma32(cat(*(const half4*)v1, *(const half4*)(v1 + 8)), pb, oacc1);
+        }
+    };
+
+    // One key tile j.  cur holds tile j's scores; the step forms tile j + 1's
+    // scores into nxt and adds tile j - 1's products (P in pprev) to O while
+    // it turns cur into P (pcur), then restages and synchronises.
+    auto step = [&](int j, f32x16& cur0, f32x16& cur1, f32x16& nxt0, f32x16& nxt1,
+                    const uint32_t (&pprev)[16], uint32_t (&pcur)[16]) {
+        // Global loads in flight during this tile: K_{j+2} and V_{j+1}.
+        const bool more_k = j + 2 < n_kt, more_v = j + 1 < n_kt;
+        uint4 ka, kb, va, vb;
+        if (more_k) load_k(j + 2, ka, kb);
+        if (more_v) load_v(j + 1, va, vb);
+
+        if (j < n_kt_w) {
+            apply_rescale();
             // Mask: key past the query (causal) or at/past the length; only
             // tiles that reach past the wave's first query or the length.
             const int key0 = j * kTile;
@@ -152,72 +232,106 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
                     const int k0 = key0 + 8 * (r >> 2) + 4 * hi + (r & 3), k1 = k0 + 32;
                     const bool m0 = (CAUSAL && k0 > q) || (VARLEN && (k0 >= len || q >= len));
                     const bool m1 = (CAUSAL && k1 > q) || (VARLEN && (k1 >= len || q >= len));
-                    s0[r] = m0 ? kNegInf : s0[r];
-                    s1[r] = m1 ? kNegInf : s1[r];
+                    cur0[r] = m0 ? kNegInf : cur0[r];
+                    cur1[r] = m1 ? kNegInf : cur1[r];
                 }
             }
+
+            // Matrix-core work of this step.  Tile j + 1's scores come from
+            // the other K buffer; after the wave's last tile they are formed
+            // from whatever it holds and never used.  At j = 0 there is no
+            // previous tile: pprev is zero and V^T tile 0 stands in.
+            scores(kls[(j + 1) & 1], nxt0, nxt1);
+            pv(vls[j == 0 ? 0 : (j + 2) % 3], pprev);
+
             // Row maximum of the raw scores (c > 0, so max(S) c = max(S c)).
-            float mx = fmaxf(s0[0], s1[0]);
+            float mx = fmaxf(cur0[0], cur1[0]);
 #pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-            mx = max_halves(mx);
-            const float m_new = fmaxf(m, mx * c);
-            // A row with no admitted key yet keeps m = -inf; exponents use 0.
+            for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, cur0[r]), cur1[r]);
+            const float mxc = max_halves(mx) * c;
+            // The exponents' maximum moves (for every row of the wave) only
+            // when some row exceeds it by more than the slack; a row with no
+            // admitted key so far has m = -inf and always counts as exceeding.
+            const bool grow = __builtin_amdgcn_ballot_w64(mxc > m + kMaxSlack) != 0;
+            const float m_new = grow ? fmaxf(m, mxc) : m;
             const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
             const float neg_m = -m_use;
-            // P = 2^(S c - m'), the row's partial sum, and P^T packed as the
-            // B operand of the four 16-key k-steps (k-step s: block s / 2,
-            // accumulator rows 8 (s % 2) .. + 7).
-            uint32_t w[16];
+            // P = 2^(S c - m), the row's partial sum, and P^T packed as the B
+            // operand of the four 16-key k-steps.
             float psum = 0.0f;
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
-                const float p0 = exp2_fast(__builtin_fmaf(s0[r], c, neg_m));
-                const float p1 = exp2_fast(__builtin_fmaf(s0[r + 1], c, neg_m));
-                const float p2 = exp2_fast(__builtin_fmaf(s1[r], c, neg_m));
-                const float p3 = exp2_fast(__builtin_fmaf(s1[r + 1], c, neg_m));
+                const float p0 = exp2_fast(__builtin_fmaf(cur0[r], c, neg_m));
+                const float p1 = exp2_fast(__builtin_fmaf(cur0[r + 1], c, neg_m));
+                const float p2 = exp2_fast(__builtin_fmaf(cur1[r], c, neg_m));
+                const float p3 = exp2_fast(__builtin_fmaf(cur1[r + 1], c, neg_m));
                 psum += (p0 + p1) + (p2 + p3);
-                w[r >> 1] = pack_half2(p0, p1);
-                w[8 + (r >> 1)] = pack_half2(p2, p3);
+                pcur[r >> 1] = pack_half2(p0, p1);
+                pcur[8 + (r >> 1)] = pack_half2(p2, p3);
             }
-            // Rescale l and O when some row's maximum grew (2^(m - m') = 1 otherwise).
-            if (__builtin_amdgcn_ballot_w64(m_new != m) != 0) {
-                const float alpha = exp2_fast(m - m_use);
-                lsum *= alpha;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    oacc0[r] *= alpha;
-                    oacc1[r] *= alpha;
-                }
-            }
-            lsum += psum;
+            // l moves to the new maximum now, O (which still lacks tile
+            // j - 1's products) at the start of the next step.
+            alpha = grow ? exp2_fast(m - m_use) : 1.0f;
+            rescale = grow;
+            lsum = __builtin_fmaf(lsum, alpha, psum);
             m = m_new;
-            // O^T += V^T P^T.  k-step s covers the tile's keys 16 s + 4 hi
-            // + 0..3 and 16 s + 8 + 4 hi + 0..3 (the accumulator's order).
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const half8 pb = half8_from_words(w[4 * s], w[4 * s + 1], w[4 * s + 2], w[4 * s + 3]);
-                const half_t* v0 = Vs + l32 * kLdsRow + 16 * s + 4 * hi;
-                const half_t* v1 = v0 + 32 * kLdsRow;
-                oacc0 = mfma32(cat(*(const half4*)v0, *(const half4*)(v0 + 8)), pb, oacc0);
-                oacc1 = mfma32(cat(*(const half4*)v1, *(const half4*)(v1 + 8)), pb, oacc1);
-            }
+            SA_FWD_INTERLEAVE();
         }
 
-        if (j + 1 < n_kt) SA_FWD_STORE(j + 1, buf ^ 1);
+        // K_{j+2} replaces K_j (last read in the previous step) and V_{j+1}
+        // replaces V_{j-2} (last read in the previous step).
+        if (more_k) store_k(j & 1, ka, kb);
+        if (more_v) store_v(j + 1, (j + 1) % 3, va, vb);
+        vm_wait_all();  // nothing is outstanding here; keeps the compiler's count exact
         __syncthreads();
-    }
-#undef SA_FWD_LOAD
-#undef SA_FWD_STORE
+    };
 
-    if (!wave_rows) return;
+    // Prologue: K_0, V_0, K_1 staged; tile 0's scores formed.
+    {
+        uint4 ka, kb, va, vb;
+        if (n_kt > 0) {
+            load_k(0, ka, kb);
+            load_v(0, va, vb);
+            store_k(0, ka, kb);
+            store_v(0, 0, va, vb);
+            if (n_kt > 1) {
+                load_k(1, ka, kb);
+                store_k(1, ka, kb);
+            }
+        }
+    }
+    __syncthreads();
+    // Every global load issued so far (Q, the staged tiles) has landed: say so
+    // to the compiler, which otherwise carries them as possibly outstanding
+    // into the loop and waits on the loop's own prefetches before each tile.
+    vm_wait_all();
+
+    // Two register sets alternate roles from tile to tile, so nothing is copied.
+    f32x16 sa0, sa1, sb0, sb1;
+    uint32_t pa[16], pb[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pb[i] = 0u;
+    if (n_kt_w > 0) scores(kls[0], sa0, sa1);
+    for (int j = 0; j < n_kt; j += 2) {
+        step(j, sa0, sa1, sb0, sb1, pb, pa);
+        if (j + 1 < n_kt) step(j + 1, sb0, sb1, sa0, sa1, pa, pb);
+    }
+    // The wave's last tile's products (its V^T buffer is not restaged after it).
+    if (n_kt_w > 0) {
+        const int jl = n_kt_w - 1;
+        apply_rescale();
+        if (jl & 1) pv(vls[jl % 3], pb);
+        else pv(vls[jl % 3], pa);
+    }
+
+    if (wave_rows) {
     // Epilogue: l over both halves, O / l, L = m + log2 l; rows with no
     // admitted key (l = 0) get O = 0 and L = -inf.  O goes through this
     // wave's own LDS rows so that the stores are whole 128-byte rows.
     const float l_tot = sum_halves(lsum);
     const bool empty = !(l_tot > 0.0f);
     const float inv = empty ? 0.0f : rcp_fast(l_tot);
-    half_t* ow = &lds[0][0][0] + wave * 32 * kLdsRow;  // 32 rows x 72 halves per wave
+    half_t* ow = &kls[0][0] + wave * 32 * kLdsRow;  // 32 rows x 72 halves per wave (kls is 2 x 64 rows)
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
         uint2 v0 = make_uint2(pack_half2(oacc0[4 * rg] * inv, oacc0[4 * rg + 1] * inv),
@@ -238,19 +352,27 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
         *(uint4*)(O + (((size_t)b * T + qw + row) * H + h) * kHeadDim + col) = v;
     }
     if (hi == 0) L[((size_t)b * H + h) * T + q] = empty ? kNegInf : m + log2_fast(l_tot);
+    }  // wave_rows
+    };
+    process(items[0]);
+    if (n_items == 2) {
+        __syncthreads();  // the first item's epilogue staged O in kls
+        process(items[1]);
+    }
 }
 
 }  // namespace
 
 size_t forward_blocks(const Shape& sh) {
-    return (size_t)((sh.T + kFwdRows - 1) / kFwdRows) * sh.batch * sh.heads;
+    const size_t n_qtiles = (size_t)((sh.T + kFwdRows - 1) / kFwdRows);
+    return (sh.block_order == 0 ? (n_qtiles + 1) / 2 : n_qtiles) * sh.batch * sh.heads;
 }
 
 hipError_t launch_forward(const Shape& sh, const void* Q, const void* K, const void* Vt, void* O, float* L,
                           float c, hipStream_t stream) {
     const int n_qtiles = (sh.T + kFwdRows - 1) / kFwdRows;
     const int BH = sh.batch * sh.heads;
-    dim3 grid((unsigned)(n_qtiles * BH)), block(kFwdThreads);
+    dim3 grid((unsigned)forward_blocks(sh)), block(kFwdThreads);
     auto args = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, stream, (const half_t*)Q, (const half_t*)K, (const half_t*)Vt,
                            (half_t*)O, L, sh.seqlens, c, sh.T, sh.heads, sh.kv_heads, n_qtiles, BH,

@@ -37,6 +37,7 @@ SMALL = [
     # name, B, T, H, KV, causal, seqlens
     ("mha_t128_causal", 1, 128, 1, 1, True, None),
     ("gqa2_t320_causal_odd_tiles", 2, 320, 4, 2, True, None),
+    ("gqa2_t320_b4_causal_xcd_groups", 4, 320, 4, 2, True, None),
     ("gqa3_t192_causal", 1, 192, 6, 2, True, None),
     ("gqa8_t256_causal", 1, 256, 8, 1, True, None),
     ("mha_t128_full", 1, 128, 2, 2, False, None),
