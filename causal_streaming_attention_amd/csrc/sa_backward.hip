@@ -392,6 +392,21 @@ constexpr int kDqRows = 32 * kDqWaves;
 constexpr int kDqThreads = 64 * kDqWaves;
 constexpr int kKTileHalves = kTile * kHeadDim;  // unpadded, chunk-swizzled
 
+// dS tiles in flight per wave: the pass streams dS once from HBM, and the
+// registers are the deepest buffer the chip has (five tiles are 80 VGPRs).
+// K tiles travel with the same lead, straight into LDS (one buffer per tile
+// in flight).  The hardware counts a wave's outstanding loads in issue order,
+// so waiting for a K tile also waits for every dS load issued before it:
+// only when both streams have the same lead does that wait cost nothing.
+constexpr int kDqDepth = 5;
+constexpr int kDqLead = kDqDepth - 1;             // tiles loaded ahead of use
+constexpr int kDqVmPerStep = 2 + 4;               // per lane: K DMA, dS loads
+// Loads issued after K tile kt + 1's DMA when step kt ends: that tile's four
+// dS loads and the four steps since.  Waiting until no more than this many
+// are outstanding means the tile has landed in LDS.
+constexpr int kDqKWait = 4 + (kDqLead - 1) * kDqVmPerStep;
+static_assert(kDqKWait == 22, "the s_waitcnt immediate below");
+
 template <bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __restrict__ K,
                                                                const half_t* __restrict__ dS,
@@ -399,120 +414,170 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
                                                                const int32_t* __restrict__ seqlens, float s,
                                                                int T, int H, int KV, int n_qblk, int BH,
                                                                int block_order, long long tiles_per_head) {
-    __shared__ __attribute__((aligned(16))) half_t lds[2][kKTileHalves];  // K tiles
+    __shared__ __attribute__((aligned(16))) half_t lds[kDqDepth][kKTileHalves];  // K tiles
 
     const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int l32 = lane & 31, hi = lane >> 5;
-    int qblk, bh;
+    // Block -> (batch*head, query blocks).  Order 0: the pair (n - 1 - p, p),
+    // whose causal walks add up to the same length, with the heads of one kv
+    // head kept on one XCD.  Order 1: one query block per block, plain order.
+    int bh, n_items, items[2];
     if (block_order == 0) {
-        qblk = n_qblk - 1 - (int)(blockIdx.x / BH);
-        bh = (int)(blockIdx.x % BH);
+        int pair;
+        pair_schedule((int)blockIdx.x, (BH / H) * KV, H / KV, pair, bh);
+        items[0] = n_qblk - 1 - pair;
+        items[1] = pair;
+        n_items = pair < items[0] ? 2 : 1;
     } else {
-        qblk = (int)(blockIdx.x % n_qblk);
+        items[0] = items[1] = (int)(blockIdx.x % n_qblk);
         bh = (int)(blockIdx.x / n_qblk);
+        n_items = 1;
     }
     const int b = bh / H, h = bh % H, kv = h / (H / KV);
     const int nt = T / kTile;
     const int len = VARLEN ? min(max(seqlens[b], 0), T) : T;
     const int ntl = VARLEN ? (len + kTile - 1) / kTile : nt;  // dS tile rows/cols in use
-    const int qt0 = 2 * qblk;
-    const int qt_w = qt0 + (wave >> 1), qh = wave & 1;
-    const int q = qblk * kDqRows + 32 * wave + l32;
-    const bool wave_rows = qt_w < nt;
-
-    int kt_end = CAUSAL ? min(qt0 + 2, nt) : nt;
-    if (VARLEN) kt_end = min(kt_end, ntl);
-    if (VARLEN && qt0 >= ntl) kt_end = 0;
-    // Key tiles this wave reads: its dS row's tiles that exist.
-    const int kt_end_w = wave_rows && qt_w < ntl ? (CAUSAL ? min(qt_w + 1, kt_end) : kt_end) : 0;
-
     const half_t* Kp = K + ((size_t)b * KV + kv) * (size_t)T * kHeadDim;
-    // This lane's dS words of tile (qt_w, kt): quadrant (qh, kh) at 1024 kh,
-    // key octet kc = 2 (s % 2) + hi at 256 kc, query l32 at 8 l32.
-    const half_t* dSw = dS + ((size_t)b * H + h) * (size_t)tiles_per_head * (kTile * kTile) +
-                        (size_t)(2 * qh) * 1024 + (size_t)hi * 256 + 8 * l32 +
-                        (CAUSAL ? (size_t)qt_w * (qt_w + 1) / 2 : (size_t)qt_w * nt) * (kTile * kTile);
 
-    // K staging: thread tid moves 16-byte chunks (row_a, c) and (row_a + 32, c),
-    // stored at chunk c ^ swz_key(row) of the row.
-    const int row_a = tid >> 3, row_b = row_a + 32, chk = tid & 7;
-    const int st_a = row_a * kHeadDim + ((chk ^ swz_key(row_a)) << 3);
-    const int st_b = row_b * kHeadDim + ((chk ^ swz_key(row_b)) << 3);
-    uint4 k1a, k1b, k2a, k2b;  // K tiles kt + 1 and kt + 2 in flight
-    auto load_k = [&](int kt, uint4& ra, uint4& rb) {
-        const half_t* kt_ = Kp + (size_t)(kt * kTile) * kHeadDim + chk * 8;
-        ra = *(const uint4*)(kt_ + row_a * kHeadDim);
-        rb = *(const uint4*)(kt_ + row_b * kHeadDim);
+    // K DMA: wave w moves rows 8 (2 w + u) + lane / 8 (u = 0, 1) of a tile; a
+    // lane's 16 bytes land at slot lane % 8 of its row, so it fetches the
+    // row's chunk (lane % 8) ^ swz_key(row): LDS holds chunk c of a row at
+    // c ^ swz_key(row).
+    const int dma_row0 = 16 * wave + (lane >> 3), dma_row1 = dma_row0 + 8;
+    const int dma_c0 = (lane & 7) ^ swz_key(dma_row0), dma_c1 = (lane & 7) ^ swz_key(dma_row1);
+    auto dma_k = [&](int kt, int buf) {
+        const half_t* src = Kp + (size_t)(kt * kTile) * kHeadDim;
+        dma16(src + dma_row0 * kHeadDim + dma_c0 * 8, (char*)&lds[buf][(16 * wave) * kHeadDim]);
+        dma16(src + dma_row1 * kHeadDim + dma_c1 * 8, (char*)&lds[buf][(16 * wave + 8) * kHeadDim]);
     };
-    auto store_k = [&](int kt, int buf, uint4 ra, uint4 rb) {
-        if (VARLEN && kt * kTile + row_a >= len) ra = make_uint4(0, 0, 0, 0);  // padded keys
-        if (VARLEN && kt * kTile + row_b >= len) rb = make_uint4(0, 0, 0, 0);
-        *(uint4*)&lds[buf][st_a] = ra;
-        *(uint4*)&lds[buf][st_b] = rb;
-    };
-    half8 b0[4], b1[4], b2[4], b3[4];  // dS operands of tiles kt .. kt + 3
-    auto load_s = [&](int kt, half8* dst) {
-        const half_t* t_ = dSw + (size_t)kt * (kTile * kTile);
-        dst[0] = *(const half8*)(t_);
-        dst[1] = *(const half8*)(t_ + 512);
-        dst[2] = *(const half8*)(t_ + 1024);
-        dst[3] = *(const half8*)(t_ + 1536);
-    };
-
-    f32x16 acc0 = zero16(), acc1 = zero16();
-    if (kt_end > 0) {
-        uint4 ra, rb;
-        load_k(0, ra, rb);
-        store_k(0, 0, ra, rb);
-        if (kt_end > 1) load_k(1, k1a, k1b);
-    }
-    if (kt_end_w > 0) load_s(0, b0);
-    if (kt_end_w > 1) load_s(1, b1);
-    if (kt_end_w > 2) load_s(2, b2);
-    __syncthreads();
     const int trr = (lane & 15) >> 2, trc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    for (int kt = 0; kt < kt_end; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 2 < kt_end) load_k(kt + 2, k2a, k2b);
-        if (kt + 3 < kt_end_w) load_s(kt + 3, b3);
-        if (kt < kt_end_w) {
-            const half_t* Ks = lds[buf];
+
+    auto process = [&](const int qblk) {
+        const int qt0 = 2 * qblk;
+        const int qt_w = qt0 + (wave >> 1), qh = wave & 1;
+        const int q = qblk * kDqRows + 32 * wave + l32;
+        const bool wave_rows = qt_w < nt;
+
+        int kt_end = CAUSAL ? min(qt0 + 2, nt) : nt;
+        if (VARLEN) kt_end = min(kt_end, ntl);
+        if (VARLEN && qt0 >= ntl) kt_end = 0;
+        // Key tiles this wave reads: its dS row's tiles that exist.
+        const int kt_end_w = wave_rows && qt_w < ntl ? (CAUSAL ? min(qt_w + 1, kt_end) : kt_end) : 0;
+        const int kt_clamp = max(kt_end - 1, 0);
+
+        // This lane's dS words of tile (qt_w, kt): quadrant (qh, kh) at 1024 kh,
+        // key octet kc = 2 (s % 2) + hi at 256 kc, query l32 at 8 l32.  Loads
+        // are issued on every path (see below), so their tile is clamped into
+        // the workspace: row qt_l, key tiles up to kt_last.
+        const int qt_l = min(qt_w, nt - 1);
+        const int kt_last = CAUSAL ? qt_l : nt - 1;
+        const half_t* dSw = dS + ((size_t)b * H + h) * (size_t)tiles_per_head * (kTile * kTile) +
+                            (size_t)(2 * qh) * 1024 + (size_t)hi * 256 + 8 * l32 +
+                            (CAUSAL ? (size_t)qt_l * (qt_l + 1) / 2 : (size_t)qt_l * nt) * (kTile * kTile);
+        auto load_s = [&](int kt, half8 (&dst)[4]) {
+            const half_t* t_ = dSw + (size_t)min(kt, kt_last) * (kTile * kTile);
+            dst[0] = gload16_async(t_);
+            dst[1] = gload16_async(t_ + 512);
+            dst[2] = gload16_async(t_ + 1024);
+            dst[3] = gload16_async(t_ + 1536);
+        };
+        // Every step issues K's DMA then the dS loads, on every path, so a
+        // wave's count of loads younger than any given one is fixed: the
+        // waits below name it.  (The dS loads are invisible to the compiler,
+        // whose own wait placement loses track of loop-carried loads.)
+        auto issue = [&](int kt, half8 (&dst)[4]) {
+            dma_k(min(kt, kt_clamp), kt % kDqDepth);
+            asm volatile("" ::: "memory");
+            load_s(kt, dst);
+        };
+
+        f32x16 acc0 = zero16(), acc1 = zero16();
+        // dS tile kt lives in register slot kt % 5 from step kt - 4 to step kt.
+        half8 sl0[4], sl1[4], sl2[4], sl3[4], sl4[4];
+        issue(0, sl0);
+        issue(1, sl1);
+        issue(2, sl2);
+        issue(3, sl3);
+        asm volatile("s_waitcnt vmcnt(22)" ::: "memory");  // K tile 0 (and older) landed
+        __builtin_amdgcn_s_barrier();
+
+        auto step = [&](const int kt, half8 (&cur)[4], half8 (&ahead)[4]) {
+            issue(kt + kDqLead, ahead);
+            if (kt >= kt_end) return;  // padding step of the unrolled loop: loads only
+            if (kt < kt_end_w) {
+                // dS tile kt, issued four steps back: 24 loads are younger.
+                static_assert((kDqLead) * kDqVmPerStep == 24, "the s_waitcnt immediate below");
+                asm volatile("s_waitcnt vmcnt(24)" : "+v"(cur[0]), "+v"(cur[1]), "+v"(cur[2]), "+v"(cur[3]));
+                const half_t* Ks = lds[kt % kDqDepth];
+                half4 t[16];
 #pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-                // A = K^T: lane (d, hi) holds K[16 s4 + 8 hi + 0..7][d].
-                const int r0 = 16 * s4 + 8 * hi + trr;
-                const half8 a0 = cat(lds_read_tr(Ks + r0 * kHeadDim + (((trc >> 3) ^ swz_key(r0)) << 3) + (trc & 7)),
-                                     lds_read_tr(Ks + (r0 + 4) * kHeadDim +
-                                                 (((trc >> 3) ^ swz_key(r0 + 4)) << 3) + (trc & 7)));
-                const half8 a1 = cat(lds_read_tr(Ks + r0 * kHeadDim +
-                                                 ((((trc + 32) >> 3) ^ swz_key(r0)) << 3) + (trc & 7)),
-                                     lds_read_tr(Ks + (r0 + 4) * kHeadDim +
-                                                 ((((trc + 32) >> 3) ^ swz_key(r0 + 4)) << 3) + (trc & 7)));
-                acc0 = mfma32(a0, b0[s4], acc0);
-                acc1 = mfma32(a1, b0[s4], acc1);
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    // A = K^T: lane (d, hi) holds K[16 s4 + 8 hi + 0..7][d].
+                    const int r0 = 16 * s4 + 8 * hi + trr;
+                    t[4 * s4 + 0] = lds_read_tr_async(Ks + r0 * kHeadDim + (((trc >> 3) ^ swz_key(r0)) << 3) + (trc & 7));
+                    t[4 * s4 + 1] = lds_read_tr_async(Ks + (r0 + 4) * kHeadDim +
+                                                      (((trc >> 3) ^ swz_key(r0 + 4)) << 3) + (trc & 7));
+                    t[4 * s4 + 2] = lds_read_tr_async(Ks + r0 * kHeadDim +
+                                                      ((((trc + 32) >> 3) ^ swz_key(r0)) << 3) + (trc & 7));
+                    t[4 * s4 + 3] = lds_read_tr_async(Ks + (r0 + 4) * kHeadDim +
+                                                      ((((trc + 32) >> 3) ^ swz_key(r0 + 4)) << 3) + (trc & 7));
+                }
+                lds_wait(t[0], t[1], t[2], t[3], t[4], t[5], t[6], t[7]);
+                lds_wait(t[8], t[9], t[10], t[11], t[12], t[13], t[14], t[15]);
+                if (VARLEN && (kt + 1) * kTile > len) {
+                    // Keys at or past the length: the DMA brought whatever
+                    // the padding holds; their dS is zero, so zero K too.
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int key = kt * kTile + 16 * s4 + 8 * hi + 4 * (e & 1) + 0;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                if (key + i >= len) t[4 * s4 + e][i] = (half_t)0.0f;
+                        }
+                }
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    acc0 = mfma32(cat(t[4 * s4 + 0], t[4 * s4 + 1]), cur[s4], acc0);
+                    acc1 = mfma32(cat(t[4 * s4 + 2], t[4 * s4 + 3]), cur[s4], acc1);
+                }
             }
+            // K tile kt + 1 (and every older load) has landed in LDS; every
+            // wave is done reading buffer kt % 5 before it is refilled.
+            asm volatile("s_waitcnt vmcnt(22)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+        };
+        static_assert(kDqDepth == 5, "five unrolled steps below");
+        for (int kt = 0; kt < kt_end; kt += kDqDepth) {
+            step(kt, sl0, sl4);
+            step(kt + 1, sl1, sl0);
+            step(kt + 2, sl2, sl1);
+            step(kt + 3, sl3, sl2);
+            step(kt + 4, sl4, sl3);
         }
-        if (kt + 1 < kt_end) store_k(kt + 1, buf ^ 1, k1a, k1b);
-        k1a = k2a;
-        k1b = k2b;
+        if (!wave_rows) return;
+        float* dq = dQ + (((size_t)b * H + h) * T + q) * kHeadDim;
+        const float scale = (!VARLEN || q < len) ? s : 0.0f;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            b0[u] = b1[u];
-            b1[u] = b2[u];
-            b2[u] = b3[u];
+        for (int rg = 0; rg < 4; ++rg) {
+            f32x4 v0 = {acc0[4 * rg], acc0[4 * rg + 1], acc0[4 * rg + 2], acc0[4 * rg + 3]};
+            f32x4 v1 = {acc1[4 * rg], acc1[4 * rg + 1], acc1[4 * rg + 2], acc1[4 * rg + 3]};
+            *(f32x4*)(dq + 8 * rg + 4 * hi) = v0 * scale;
+            *(f32x4*)(dq + 32 + 8 * rg + 4 * hi) = v1 * scale;
         }
-        __syncthreads();
+    };
+    process(items[0]);
+    if (n_items == 2) {
+        // Every DMA of the first item must land before the second refills
+        // its buffers, and every wave must be past its last read.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        process(items[1]);
     }
-    if (!wave_rows) return;
-    float* dq = dQ + (((size_t)b * H + h) * T + q) * kHeadDim;
-    const float scale = (!VARLEN || q < len) ? s : 0.0f;
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-        f32x4 v0 = {acc0[4 * rg], acc0[4 * rg + 1], acc0[4 * rg + 2], acc0[4 * rg + 3]};
-        f32x4 v1 = {acc1[4 * rg], acc1[4 * rg + 1], acc1[4 * rg + 2], acc1[4 * rg + 3]};
-        *(f32x4*)(dq + 8 * rg + 4 * hi) = v0 * scale;
-        *(f32x4*)(dq + 32 + 8 * rg + 4 * hi) = v1 * scale;
-    }
+    // The padding steps leave DMAs into this workgroup's LDS and loads into
+    // this wave's registers in flight: both must land before the wave ends.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 template <bool CAUSAL, bool VARLEN>
@@ -548,7 +613,8 @@ size_t row_terms_blocks(const Shape& sh) {
 }
 size_t key_pass_blocks(const Shape& sh) { return (size_t)sh.batch * sh.kv_heads * (sh.T / kTile); }
 size_t dq_pass_blocks(const Shape& sh) {
-    return (size_t)sh.batch * sh.heads * ((sh.T + kDqRows - 1) / kDqRows);
+    const size_t n_qblk = (size_t)((sh.T + kDqRows - 1) / kDqRows);
+    return (size_t)sh.batch * sh.heads * (sh.block_order == 0 ? (n_qblk + 1) / 2 : n_qblk);
 }
 
 hipError_t launch_row_terms(const Shape& sh, const void* dO, const void* O, float* D, hipStream_t stream) {

@@ -123,6 +123,14 @@ __device__ __forceinline__ half4 lds_read_tr_async(const half_t* p) {
     asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
     return r;
 }
+// A 16-byte global load the compiler does not track: the caller must wait for
+// it with an s_waitcnt vmcnt that ties the result (asm "+v"), counting every
+// vector memory instruction issued after it.
+__device__ __forceinline__ half8 gload16_async(const void* p) {
+    half8 r;
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+    return r;
+}
 // Wait for every outstanding LDS read of this wave; the operands are tied so
 // no use of them can be scheduled before the wait.
 __device__ __forceinline__ void lds_wait(half4& a, half4& b, half4& c, half4& d, half4& e, half4& f, half4& g,
