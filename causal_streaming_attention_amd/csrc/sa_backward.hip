@@ -208,10 +208,14 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     // Items in order: for each of the slot's heads, sub-tiles from the last down.
     int head = kv * G + slot, sub = sub_hi - 1;
     if (n_items > 0) issue_item(head, sub, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the first item has landed in LDS
 
     for (int it = 0; it < n_items; ++it) {
         const int buf = it & 1;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this item has landed in LDS
+        // This item's loads were issued at the top of the previous item, and
+        // only that item's two dS stores are younger: wait for the loads, not
+        // for the stores to reach memory.
+        asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
         int next_head = head, next_sub = sub - 1;
         if (next_sub < sub_lo) {
             next_sub = sub_hi - 1;
@@ -284,9 +288,11 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
         // dS to global: through this wave's LDS block [key][query], read back
         // transposed so that lane l holds 8 consecutive keys of query l % 32,
         // and stored as two fully coalesced 1 KB runs.
+        // (asm writes: the compiler would otherwise wait for the next item's
+        // direct-to-LDS loads, which it cannot tell apart from dsx, first.)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg)
-            *(uint2*)(dsx + l32 * kDsxRow + 8 * rg + 4 * hi) = make_uint2(wd[2 * rg], wd[2 * rg + 1]);
+            lds_write8_async(dsx + l32 * kDsxRow + 8 * rg + 4 * hi, make_uint2(wd[2 * rg], wd[2 * rg + 1]));
         {
             half4 x0 = lds_read_tr_async(dsx + tr_offset(lane, 0, 8, 0, kDsxRow));
             half4 x1 = lds_read_tr_async(dsx + tr_offset(lane, 4, 12, 0, kDsxRow));

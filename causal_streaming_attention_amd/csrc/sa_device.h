@@ -123,6 +123,12 @@ __device__ __forceinline__ half4 lds_read_tr_async(const half_t* p) {
     asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
     return r;
 }
+// An 8-byte LDS write the compiler does not see as one (no waits are placed
+// for it); a later asm LDS read and its lgkmcnt wait order after it.
+__device__ __forceinline__ void lds_write8_async(half_t* p, uint2 v) {
+    const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) half_t*)(p);
+    asm volatile("ds_write_b64 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
 // A 16-byte global load the compiler does not track: the caller must wait for
 // it with an s_waitcnt vmcnt that ties the result (asm "+v"), counting every
 // vector memory instruction issued after it.
