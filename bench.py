@@ -80,23 +80,32 @@ def load_traffic(kernel: str, workload: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, x):
-    """Time the binary64 oracle on the first K/V head group (its G query heads, first
-    sequence) of the same inputs: the whole forward and backward of that group, i.e.
-    1 / (batch * kv_heads) of the job, reported in the workload's FLOP convention."""
+def cpu_baseline(w, x, budget_s: float = 10.0):
+    """Time the binary64 oracle on the same inputs, one K/V head group (its G query
+    heads of one sequence, the whole forward and backward) at a time, until about
+    `budget_s` seconds of CPU work are done or every group has run; reported in the
+    workload's FLOP convention."""
     import oracle
     from causal_streaming_attention_amd.workloads import SCALE
     G = w.heads // w.kv_heads
-    sl = None if x["seqlens"] is None else x["seqlens"][:1]
-    part = {"Q": x["Q"][:1, :G], "K": x["K"][:1, :1], "Vt": x["Vt"][:1, :1], "dO": x["dO"][:1, :G]}
-    t0 = time.perf_counter()
-    oracle.backward(part["Q"], part["K"], part["Vt"], part["dO"], s=SCALE, causal=w.causal, seqlens=sl)
-    dt = time.perf_counter() - t0
-    n = w.T if sl is None else int(sl[0])
-    flops = 14 * HEAD_DIM * (n * float(n) * (0.5 if w.causal else 1.0)) * G
+    groups = [(b, kv) for b in range(w.batch) for kv in range(w.kv_heads)]
+    flops, dt, done = 0.0, 0.0, 0
+    for b, kv in groups:
+        sl = None if x["seqlens"] is None else x["seqlens"][b:b + 1]
+        t0 = time.perf_counter()
+        oracle.backward(x["Q"][b:b + 1, kv * G:(kv + 1) * G], x["K"][b:b + 1, kv:kv + 1],
+                        x["Vt"][b:b + 1, kv:kv + 1], x["dO"][b:b + 1, kv * G:(kv + 1) * G],
+                        s=SCALE, causal=w.causal, seqlens=sl)
+        dt += time.perf_counter() - t0
+        n = w.T if sl is None else int(sl[0])
+        flops += 14 * HEAD_DIM * (n * float(n) * (0.5 if w.causal else 1.0)) * G
+        done += 1
+        if dt >= budget_s:
+            break
+    what = "the whole job" if done == len(groups) else f"{done} of {len(groups)} groups"
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"one K/V head group ({G} query heads, batch 1, T={w.T}) of {w.name}: full forward "
-                      f"and backward, {flops / 1e9:.2f} GFLOP in {dt:.1f} s (1/{w.batch * w.kv_heads} of the job)",
+            "sample": f"{what} of {w.name} (K/V head groups of {G} query heads, batch row by batch row): "
+                      f"full forward and backward, {flops / 1e9:.2f} GFLOP in {dt:.1f} s",
             "cpu": platform.processor() or _cpu_model()}
 
 
