@@ -37,7 +37,7 @@ HBM_PEAK_GBS = 8000.0
 HEAD_DIM = 64
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "causal_streaming_attention_amd", "csrc", f)
-                  for f in ("sa_device.h", "sa_forward.hip", "sa_backward.hip")]
+                  for f in ("sa_device.h", "sa_forward.hip", "sa_backward.hip", "sa_query.hip")]
 
 
 def kernel_source_hash() -> str:
@@ -282,6 +282,35 @@ def main():
             e["frac_hbm_peak"] = round(gbs / HBM_PEAK_GBS, 4)
         kernels[n] = e
 
+    # The two-launch backward (query pass for D and dQ, key pass storing no
+    # dS), timed the same way beside the three-launch path.
+    def step2(ev=None):
+        if ev: ev[0].record(stream)
+        sa.sa_forward_ex(sh, buf.Q, buf.K, buf.Vt, buf.O, buf.L, c, stream)
+        if ev: ev[1].record(stream)
+        sa.sa_query_pass(sh, buf.dO, buf.O, buf.L, buf.Q, buf.K, buf.Vt, c, SCALE, buf.D, buf.dQ, stream)
+        if ev: ev[2].record(stream)
+        sa.sa_key_pass(sh, buf.Q, buf.K, buf.Vt, buf.dO, buf.L, buf.D, None, 0, c, SCALE, buf.dK, buf.dVt,
+                       stream)
+        if ev: ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step2()
+    events2 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        step2(events2[k])
+    torch.cuda.synchronize()
+    names2 = ["forward", "query_pass", "key_pass_no_ds"]
+    per2 = {n: float(np.mean([events2[k][i].elapsed_time(events2[k][i + 1]) for k in range(args.steps)]))
+            for i, n in enumerate(names2)}
+    step2_ms = float(np.mean([events2[k][0].elapsed_time(events2[k][3]) for k in range(args.steps)]))
+    two_pass = {"ms_per_step": round(step2_ms, 4),
+                "tflops": round(fl["total"] / (step2_ms * 1e-3) / 1e12, 2),
+                "kernels_ms": {n: round(per2[n], 4) for n in names2},
+                "note": "same workload and FLOP convention; the backward recomputes S, P, dP in both passes "
+                        "and stores no dS"}
+
     if args.calibrate_copy_mb > 0:
         n = args.calibrate_copy_mb << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -300,6 +329,7 @@ def main():
         "flops_per_step": fl["total"],
         "kernels": kernels,
         "roofline": roofline,
+        "two_pass_backward": two_pass,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x)

@@ -54,6 +54,8 @@ _SIGS = {
     "sa_row_terms": (_I, [_SP, _V, _V, _V, _V]),
     "sa_key_pass": (_I, [_SP, _V, _V, _V, _V, _V, _V, _V, _Z, _F, _F, _V, _V, _V]),
     "sa_dq_pass": (_I, [_SP, _V, _V, _Z, _F, _V, _V]),
+    "sa_query_pass": (_I, [_SP, _V, _V, _V, _V, _V, _V, _F, _F, _V, _V, _V]),
+    "sa_backward_two_pass": (_I, [_SP, _V, _V, _V, _V, _V, _V, _V, _F, _F, _V, _V, _V, _V]),
     "sa_status_string": (ctypes.c_char_p, [_I]),
 }
 
@@ -163,6 +165,17 @@ def sa_dq_pass(shape, K, dS, dS_bytes, s, dQ, stream=None):
                                _stream(stream)), "sa_dq_pass")
 
 
+def sa_query_pass(shape, dO, O, L, Q, K, Vt, c, s, D, dQ, stream=None):
+    _check(native().sa_query_pass(ctypes.byref(shape), _ptr(dO), _ptr(O), _ptr(L), _ptr(Q), _ptr(K), _ptr(Vt),
+                                  c, s, _ptr(D), _ptr(dQ), _stream(stream)), "sa_query_pass")
+
+
+def sa_backward_two_pass(shape, dO, O, L, D, Q, K, Vt, c, s, dQ, dK, dVt, stream=None):
+    _check(native().sa_backward_two_pass(ctypes.byref(shape), _ptr(dO), _ptr(O), _ptr(L), _ptr(D), _ptr(Q),
+                                         _ptr(K), _ptr(Vt), c, s, _ptr(dQ), _ptr(dK), _ptr(dVt),
+                                         _stream(stream)), "sa_backward_two_pass")
+
+
 class Buffers:
     """Device tensors for one problem (torch allocations; the library allocates nothing).
 
@@ -198,3 +211,7 @@ class Buffers:
     def backward(self, c, s, stream=None):
         sa_backward_ex(self.shape, self.dO, self.O, self.L, self.D, self.dS, self.ws_bytes, self.Q, self.K,
                        self.Vt, c, s, self.dQ, self.dK, self.dVt, stream)
+
+    def backward_two_pass(self, c, s, stream=None):
+        sa_backward_two_pass(self.shape, self.dO, self.O, self.L, self.D, self.Q, self.K, self.Vt, c, s,
+                             self.dQ, self.dK, self.dVt, stream)

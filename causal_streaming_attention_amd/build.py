@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["sa_api.cpp", "sa_forward.hip", "sa_backward.hip"]
+SOURCES = ["sa_api.cpp", "sa_forward.hip", "sa_backward.hip", "sa_query.hip"]
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # The kernels never form a NaN from finite inputs (masked scores are selected to -inf, empty rows
 # are tested explicitly), so maxima need no NaN canonicalization; infinities keep their meaning.

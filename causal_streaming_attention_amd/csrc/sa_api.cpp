@@ -64,7 +64,7 @@ sa_status sa_check_shape(const sa_shape* shape) {
     const sa::Shape sh = to_shape(shape);
     const size_t lim = (size_t)INT_MAX;
     if (sa::forward_blocks(sh) > lim || sa::row_terms_blocks(sh) > lim || sa::key_pass_blocks(sh) > lim ||
-        sa::dq_pass_blocks(sh) > lim)
+        sa::dq_pass_blocks(sh) > lim || sa::query_pass_blocks(sh) > lim)
         return SA_ERR_SHAPE;
     return SA_OK;
 }
@@ -102,8 +102,11 @@ sa_status sa_key_pass(const sa_shape* shape, const void* Q, const void* K, const
                       float* dVt, void* stream) {
     sa_status st = sa_check_shape(shape);
     if (st != SA_OK) return st;
-    if ((st = check_ptrs({Q, K, Vt, dO, L, D, dS, dK, dVt})) != SA_OK) return st;
-    if (dS_bytes < sa_backward_workspace_bytes(shape)) return SA_ERR_WORKSPACE;
+    if ((st = check_ptrs({Q, K, Vt, dO, L, D, dK, dVt})) != SA_OK) return st;
+    if (dS) {  // NULL: the two-launch backward's key launch, nothing stored
+        if ((st = check_ptrs({dS})) != SA_OK) return st;
+        if (dS_bytes < sa_backward_workspace_bytes(shape)) return SA_ERR_WORKSPACE;
+    }
     if (!scale_ok(c) || !scale_ok(s)) return SA_ERR_ARGUMENT;
     return from_hip(sa::launch_key_pass(to_shape(shape), Q, K, Vt, dO, L, D, dS, c, s, dK, dVt,
                                         (hipStream_t)stream));
@@ -139,6 +142,28 @@ sa_status sa_backward(const void* dO, const void* O, const float* L, float* D, v
                       int kv_heads, float* dQ, float* dK, float* dVt, void* stream) {
     sa_shape sh = batch1_causal(T, heads, kv_heads);
     return sa_backward_ex(&sh, dO, O, L, D, dS, dS_bytes, Q, K, Vt, c, s, dQ, dK, dVt, stream);
+}
+
+sa_status sa_query_pass(const sa_shape* shape, const void* dO, const void* O, const float* L, const void* Q,
+                        const void* K, const void* Vt, float c, float s, float* D, float* dQ, void* stream) {
+    sa_status st = sa_check_shape(shape);
+    if (st != SA_OK) return st;
+    if ((st = check_ptrs({dO, O, L, Q, K, Vt, D, dQ})) != SA_OK) return st;
+    if (!scale_ok(c) || !scale_ok(s)) return SA_ERR_ARGUMENT;
+    return from_hip(sa::launch_query_pass(to_shape(shape), dO, O, L, Q, K, Vt, c, s, D, dQ, (hipStream_t)stream));
+}
+
+sa_status sa_backward_two_pass(const sa_shape* shape, const void* dO, const void* O, const float* L, float* D,
+                               const void* Q, const void* K, const void* Vt, float c, float s, float* dQ,
+                               float* dK, float* dVt, void* stream) {
+    sa_status st = sa_check_shape(shape);
+    if (st != SA_OK) return st;
+    if ((st = check_ptrs({dO, O, L, D, Q, K, Vt, dQ, dK, dVt})) != SA_OK) return st;
+    if (!scale_ok(c) || !scale_ok(s)) return SA_ERR_ARGUMENT;
+    const sa::Shape sh = to_shape(shape);
+    hipStream_t strm = (hipStream_t)stream;
+    if ((st = from_hip(sa::launch_query_pass(sh, dO, O, L, Q, K, Vt, c, s, D, dQ, strm))) != SA_OK) return st;
+    return from_hip(sa::launch_key_pass(sh, Q, K, Vt, dO, L, D, nullptr, c, s, dK, dVt, strm));
 }
 
 const char* sa_status_string(int status) {

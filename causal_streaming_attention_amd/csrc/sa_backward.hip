@@ -131,6 +131,7 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int l32 = lane & 31, hi = lane >> 5;
     const int slot = wave >> 1, khalf = wave & 1;
+    const bool store_ds = dS != nullptr;
 
     int kt, bkv;
     if (block_order == 0) {  // key tile 0 first: it walks every query
@@ -209,13 +210,17 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     int head = kv * G + slot, sub = sub_hi - 1;
     if (n_items > 0) issue_item(head, sub, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the first item has landed in LDS
+    // ... and K's fragments: say so to the compiler too, which otherwise keeps
+    // them as possibly outstanding and drains every load before the products.
+    vm_wait_all();
 
     for (int it = 0; it < n_items; ++it) {
         const int buf = it & 1;
         // This item's loads were issued at the top of the previous item, and
-        // only that item's two dS stores are younger: wait for the loads, not
-        // for the stores to reach memory.
-        asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+        // only that item's two dS stores (if dS is stored) are younger: wait
+        // for the loads, not for the stores to reach memory.
+        if (store_ds) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         int next_head = head, next_sub = sub - 1;
         if (next_sub < sub_lo) {
             next_sub = sub_hi - 1;
@@ -240,13 +245,6 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
             if ((lane & 31) >= keep) Ls[lane] = 0.0f;  // L (lanes 0..31) and D (32..63)
         }
         if (it + 1 < n_items) issue_item(next_head, next_sub, buf ^ 1);
-
-        // This wave's 32x32 block of the 64x64 dS tile: quadrant (query half
-        // sub % 2, key half khalf), stored as [key octet 4][query 32][8 keys].
-        const int qt = sub >> 1;
-        const size_t tile = CAUSAL ? (size_t)qt * (qt + 1) / 2 + kt : (size_t)qt * (T / kTile) + kt;
-        half_t* dsp = dS + (((size_t)b * H + head) * (size_t)tiles_per_head + tile) * (kTile * kTile) +
-                      (size_t)(2 * (sub & 1) + khalf) * 1024 + 8 * lane;
 
         // A block with no admitted pair (the diagonal sub-tile of the upper key
         // half, padding) goes through the same code: the mask makes its P and
@@ -290,10 +288,19 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
         // and stored as two fully coalesced 1 KB runs.
         // (asm writes: the compiler would otherwise wait for the next item's
         // direct-to-LDS loads, which it cannot tell apart from dsx, first.)
+        // Without a workspace (the two-launch backward's key launch) nothing
+        // is stored.
+        if (store_ds) {
+            // This wave's 32x32 block of the 64x64 dS tile: quadrant (query
+            // half sub % 2, key half khalf), stored as [key octet 4][query 32]
+            // [8 keys].
+            const int qt = sub >> 1;
+            const size_t tile = CAUSAL ? (size_t)qt * (qt + 1) / 2 + kt : (size_t)qt * (T / kTile) + kt;
+            half_t* dsp = dS + (((size_t)b * H + head) * (size_t)tiles_per_head + tile) * (kTile * kTile) +
+                          (size_t)(2 * (sub & 1) + khalf) * 1024 + 8 * lane;
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg)
-            lds_write8_async(dsx + l32 * kDsxRow + 8 * rg + 4 * hi, make_uint2(wd[2 * rg], wd[2 * rg + 1]));
-        {
+            for (int rg = 0; rg < 4; ++rg)
+                lds_write8_async(dsx + l32 * kDsxRow + 8 * rg + 4 * hi, make_uint2(wd[2 * rg], wd[2 * rg + 1]));
             half4 x0 = lds_read_tr_async(dsx + tr_offset(lane, 0, 8, 0, kDsxRow));
             half4 x1 = lds_read_tr_async(dsx + tr_offset(lane, 4, 12, 0, kDsxRow));
             half4 x2 = lds_read_tr_async(dsx + tr_offset(lane, 16, 24, 0, kDsxRow));

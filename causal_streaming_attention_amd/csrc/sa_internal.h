@@ -30,11 +30,17 @@ hipError_t launch_key_pass(const Shape& sh, const void* Q, const void* K, const 
                            hipStream_t stream);
 hipError_t launch_dq_pass(const Shape& sh, const void* K, const void* dS, float s, float* dQ,
                           hipStream_t stream);
+// The two-launch backward's query pass (D and dQ); its key launch is
+// launch_key_pass with dS == nullptr (no score gradients stored).
+hipError_t launch_query_pass(const Shape& sh, const void* dO, const void* O, const float* L, const void* Q,
+                             const void* K, const void* Vt, float c, float s, float* D, float* dQ,
+                             hipStream_t stream);
 
 // Grid sizes, for the entry points' admission of launch dimensions.
 size_t forward_blocks(const Shape& sh);
 size_t row_terms_blocks(const Shape& sh);
 size_t key_pass_blocks(const Shape& sh);
 size_t dq_pass_blocks(const Shape& sh);
+size_t query_pass_blocks(const Shape& sh);
 
 }  // namespace sa

@@ -1,0 +1,304 @@
+// sa_query.hip -- the query pass of the two-launch backward on gfx950.
+//
+// Method: StreamingAttentionSM86 page, banner "The backward pass,
+// deterministic and in two launches (no atomics)", the query launch: a block
+// per query tile of a query head forms D = rowsum(dO * O) for its rows (and
+// writes it for the key launch), then walks the key tiles up to the diagonal
+// as the forward does, recomputing per tile
+//   S = Q K^T,  P = 2^(S c - L),  dP = dO V^T,  dS = P (dP - D),
+// and keeping dQ = s * sum over the tiles of dS K.  No score gradient leaves
+// the chip: the key launch (the key pass without its dS store) forms dK and
+// dV the same way.
+//
+// MI355X design: a 256-thread workgroup (4 wave64s) takes 128 queries of one
+// query head, each wave 32 queries, and walks the key tiles with the K tile
+// and the V^T tile staged once in LDS for the four waves (16-byte loads one
+// tile ahead, double-buffered).  Per tile a wave runs 24 products on
+// v_mfma_f32_32x32x16_f16, all in the forward's orientation (lane = query):
+//   S^T  = K Q^T    (A = K rows, LDS; B = Q^T, registers)
+//   dP^T = V dO^T   (A = V rows, read transposed from the V^T tile; B = dO^T)
+//   dQ^T += K^T dS^T (A = K^T, read transposed from the K tile in the permuted
+//                     key order of the score accumulator; B = dS^T packed to
+//                     binary16 straight from the accumulator, as the forward
+//                     feeds P to P V)
+// so P, dP and dS never leave registers.  Both tiles are stored unpadded
+// with the 16-byte chunks of each row permuted (swz), which keeps the row
+// reads and the transposed reads free of bank conflicts.
+#include "sa_device.h"
+#include "sa_internal.h"
+
+namespace sa {
+
+namespace {
+
+constexpr int kQpWaves = 4;
+constexpr int kQpRows = 32 * kQpWaves;       // queries per workgroup
+constexpr int kQpThreads = 64 * kQpWaves;
+constexpr int kQpTile = kTile * kHeadDim;    // one unpadded 64x64 tile
+
+// Row r's 16-byte chunk c of a staged tile sits at chunk c ^ key(r): key is
+// distinct over any 8 consecutive rows (16-byte row reads by 8 lanes) and
+// key / 2 is distinct within each aligned group of 4 rows (a transposed read
+// of 4 rows x 2 chunks).
+__device__ __forceinline__ int qp_key(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+__device__ __forceinline__ int qp_swz(int row, int col) {
+    return row * kHeadDim + (((col >> 3) ^ qp_key(row)) << 3) + (col & 7);
+}
+// The element a transposed read names so that lane l receives column
+// col0 + l % 32 at rows row0 + 0..3 (row0 = rowA for lanes 0..31, rowB for
+// 32..63) of a staged tile.
+__device__ __forceinline__ int qp_tr(int lane, int rowA, int rowB, int col0) {
+    const int row = ((lane & 32) ? rowB : rowA) + ((lane & 15) >> 2);
+    return qp_swz(row, col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+}
+
+// Zero the halves of an 8-half chunk at positions >= keep (keep may be <= 0 or >= 8).
+__device__ __forceinline__ uint4 qp_clear_tail(uint4 v, int keep) {
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+        if (t >= keep) w[t >> 1] &= (t & 1) ? 0x0000ffffu : 0xffff0000u;
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(kQpThreads, 2) void sa_query_kernel(
+    const half_t* __restrict__ Q, const half_t* __restrict__ K, const half_t* __restrict__ Vt,
+    const half_t* __restrict__ dO, const half_t* __restrict__ O, const float* __restrict__ L,
+    float* __restrict__ D, float* __restrict__ dQ, const int32_t* __restrict__ seqlens, float c, float s,
+    int T, int H, int KV, int n_qtiles, int BH, int block_order) {
+    __shared__ __attribute__((aligned(16))) half_t kls[2][kQpTile];  // K tiles [key][d]
+    __shared__ __attribute__((aligned(16))) half_t vls[2][kQpTile];  // V^T tiles [d][key]
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int l32 = lane & 31, hi = lane >> 5;
+
+    // Block -> (batch*head, query tiles): as the forward, the pair (n - 1 - p,
+    // p) of equal causal length with the heads of one kv head on one XCD
+    // (order 0), or one tile per block in plain order (order 1).
+    int bh, n_items, items[2];
+    if (block_order == 0) {
+        int pair;
+        pair_schedule((int)blockIdx.x, (BH / H) * KV, H / KV, pair, bh);
+        items[0] = n_qtiles - 1 - pair;
+        items[1] = pair;
+        n_items = pair < items[0] ? 2 : 1;
+    } else {
+        items[0] = items[1] = (int)(blockIdx.x % n_qtiles);
+        bh = (int)(blockIdx.x / n_qtiles);
+        n_items = 1;
+    }
+    const int b = bh / H, h = bh % H, kv = h / (H / KV);
+    const int len = VARLEN ? min(max(seqlens[b], 0), T) : T;
+    const size_t kv_off = ((size_t)b * KV + kv) * (size_t)T * kHeadDim;
+    const half_t* Kp = K + kv_off;
+    const half_t* Vp = Vt + kv_off;
+
+    // Staging: thread tid moves 16-byte chunks (row_a, cc) and (row_a + 32, cc)
+    // of a K tile (rows = keys) and of a V^T tile (rows = d, columns = keys).
+    const int row_a = tid >> 3, row_b = row_a + 32, cc = tid & 7;
+    auto load = [&](int j, uint4& ka, uint4& kb, uint4& va, uint4& vb) {
+        const half_t* kt_ = Kp + (size_t)(j * kTile) * kHeadDim + cc * 8;
+        ka = *(const uint4*)(kt_ + row_a * kHeadDim);
+        kb = *(const uint4*)(kt_ + row_b * kHeadDim);
+        va = *(const uint4*)(Vp + (size_t)row_a * T + j * kTile + cc * 8);
+        vb = *(const uint4*)(Vp + (size_t)row_b * T + j * kTile + cc * 8);
+    };
+    auto store = [&](int j, int buf, uint4 ka, uint4 kb, uint4 va, uint4 vb) {
+        if (VARLEN) {
+            // keys at or past the length: P and dS are masked to zero, and
+            // their K rows and V^T columns are cleared so that no padding
+            // value reaches a product
+            if (j * kTile + row_a >= len) ka = make_uint4(0, 0, 0, 0);
+            if (j * kTile + row_b >= len) kb = make_uint4(0, 0, 0, 0);
+            if (j * kTile + cc * 8 + 8 > len) {
+                va = qp_clear_tail(va, len - (j * kTile + cc * 8));
+                vb = qp_clear_tail(vb, len - (j * kTile + cc * 8));
+            }
+        }
+        *(uint4*)&kls[buf][qp_swz(row_a, cc * 8)] = ka;
+        *(uint4*)&kls[buf][qp_swz(row_b, cc * 8)] = kb;
+        *(uint4*)&vls[buf][qp_swz(row_a, cc * 8)] = va;
+        *(uint4*)&vls[buf][qp_swz(row_b, cc * 8)] = vb;
+    };
+
+    auto process = [&](const int qtile) {
+        const int q0 = qtile * kQpRows;
+        const int qw = q0 + 32 * wave;          // this wave's first query
+        const int q = qw + l32;                 // this lane's query
+        const bool wave_rows = qw < T;          // T % 64 == 0: whole wave in or out
+        const int row_limit = VARLEN ? len : T;
+        int kend = CAUSAL ? min(q0 + kQpRows, T) : T;
+        if (VARLEN) kend = min(kend, len);
+        const int n_kt = (kend + kTile - 1) / kTile;
+        int kend_w = CAUSAL ? qw + 32 : T;
+        if (VARLEN) kend_w = min(kend_w, len);
+        const bool wave_live = wave_rows && qw < row_limit;
+        const int n_kt_w = wave_live ? min((kend_w + kTile - 1) / kTile, n_kt) : 0;
+
+        // Q^T and dO^T as B operands: lane (query l32, half hi) holds
+        // Q[q][16 t + 8 hi + 0..7] and dO[q][16 t + 8 hi + 0..7], t = 0..3.
+        const size_t row_id = ((size_t)b * H + h) * T + q;
+        half8 qf[4], of[4];
+        float Dq = 0.0f, negL = 0.0f;
+        if (wave_live) {
+            const half_t* qp = Q + row_id * kHeadDim + 8 * hi;
+            const half_t* op = dO + row_id * kHeadDim + 8 * hi;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                qf[t] = *(const half8*)(qp + 16 * t);
+                of[t] = *(const half8*)(op + 16 * t);
+            }
+        }
+        if (wave_rows) {
+            // D = rowsum(dO * O) over this lane's 32 columns, then both halves;
+            // binary32, every fp16 widened, fused multiply-adds.  O is the
+            // forward's (token-major) output.
+            float part = 0.0f;
+            if (wave_live) {
+                const half_t* orow = O + (((size_t)b * T + q) * H + h) * kHeadDim + 8 * hi;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const half8 o8 = *(const half8*)(orow + 16 * t);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)of[t][e], (float)o8[e], part);
+                }
+            }
+            Dq = sum_halves(part);
+            if (VARLEN && q >= len) Dq = 0.0f;
+            if (hi == 0) D[row_id] = Dq;
+            negL = (VARLEN && q >= len) ? 0.0f : -L[row_id];
+        }
+
+        f32x16 dq0 = zero16(), dq1 = zero16();  // dQ^T, d blocks 0..31 and 32..63
+        if (n_kt > 0) {
+            uint4 ka, kb, va, vb;
+            load(0, ka, kb, va, vb);
+            store(0, 0, ka, kb, va, vb);
+        }
+        __syncthreads();
+        vm_wait_all();  // the staged tile and Q, dO have landed (see the forward)
+
+        for (int j = 0; j < n_kt; ++j) {
+            const int buf = j & 1;
+            const bool more = j + 1 < n_kt;
+            uint4 ka, kb, va, vb;
+            if (more) load(j + 1, ka, kb, va, vb);
+            if (j < n_kt_w) {
+                const half_t* Ks = kls[buf];
+                const half_t* Vs = vls[buf];
+                // S^T = K Q^T and dP^T = V dO^T for the tile's two 32-key blocks.
+                f32x16 s0 = zero16(), s1 = zero16(), p0 = zero16(), p1 = zero16();
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const half8 a0 = *(const half8*)(Ks + qp_swz(l32, 16 * t + 8 * hi));
+                    const half8 a1 = *(const half8*)(Ks + qp_swz(32 + l32, 16 * t + 8 * hi));
+                    s0 = mfma32(a0, qf[t], s0);
+                    s1 = mfma32(a1, qf[t], s1);
+                    // A = V: lane (key, hi) holds V^T[16 t + 8 hi + 0..7][key].
+                    const half8 v0 = cat(lds_read_tr(Vs + qp_tr(lane, 16 * t, 16 * t + 8, 0)),
+                                         lds_read_tr(Vs + qp_tr(lane, 16 * t + 4, 16 * t + 12, 0)));
+                    const half8 v1 = cat(lds_read_tr(Vs + qp_tr(lane, 16 * t, 16 * t + 8, 32)),
+                                         lds_read_tr(Vs + qp_tr(lane, 16 * t + 4, 16 * t + 12, 32)));
+                    p0 = mfma32(v0, of[t], p0);
+                    p1 = mfma32(v1, of[t], p1);
+                }
+                // P = 2^(S c - L), dS = P (dP - D); masked elements are
+                // selected to exact zeros (never multiplied: padding may hold
+                // anything).  Lane holds key 8 (r / 4) + 4 hi + r % 4 (+ 32 for
+                // the second block) of query q.
+                const int key0 = j * kTile;
+                const bool need_mask = (CAUSAL && key0 + kTile - 1 > qw) ||
+                                       (VARLEN && (key0 + kTile > len || qw + 32 > len));
+                uint32_t w[16];
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    float g[4];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const float pa = exp2_fast(__builtin_fmaf(s0[r + e], c, negL));
+                        const float pb = exp2_fast(__builtin_fmaf(s1[r + e], c, negL));
+                        g[e] = pa * (p0[r + e] - Dq);
+                        g[2 + e] = pb * (p1[r + e] - Dq);
+                    }
+                    if (need_mask) {
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const int k0 = key0 + 8 * ((r + e) >> 2) + 4 * hi + ((r + e) & 3), k1 = k0 + 32;
+                            const bool m0 = (CAUSAL && k0 > q) || (VARLEN && (k0 >= len || q >= len));
+                            const bool m1 = (CAUSAL && k1 > q) || (VARLEN && (k1 >= len || q >= len));
+                            g[e] = m0 ? 0.0f : g[e];
+                            g[2 + e] = m1 ? 0.0f : g[2 + e];
+                        }
+                    }
+                    w[r >> 1] = pack_half2(g[0], g[1]);
+                    w[8 + (r >> 1)] = pack_half2(g[2], g[3]);
+                }
+                // dQ^T += K^T dS^T.  k-step t covers the tile's keys 16 t + 4 hi
+                // + 0..3 and 16 t + 8 + 4 hi + 0..3 (the accumulator's order);
+                // K^T's A operand is read transposed in that same order.
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const half8 pb = half8_from_words(w[4 * t], w[4 * t + 1], w[4 * t + 2], w[4 * t + 3]);
+                    const half8 k0 = cat(lds_read_tr(Ks + qp_tr(lane, 16 * t, 16 * t + 4, 0)),
+                                         lds_read_tr(Ks + qp_tr(lane, 16 * t + 8, 16 * t + 12, 0)));
+                    const half8 k1 = cat(lds_read_tr(Ks + qp_tr(lane, 16 * t, 16 * t + 4, 32)),
+                                         lds_read_tr(Ks + qp_tr(lane, 16 * t + 8, 16 * t + 12, 32)));
+                    dq0 = mfma32(k0, pb, dq0);
+                    dq1 = mfma32(k1, pb, dq1);
+                }
+            }
+            if (more) store(j + 1, buf ^ 1, ka, kb, va, vb);
+            vm_wait_all();  // nothing is outstanding here; keeps the compiler's count exact
+            __syncthreads();
+        }
+
+        if (!wave_rows) return;
+        // dQ = s dQ^T: lane holds d = 8 (r / 4) + 4 hi + r % 4 of query q.
+        float* dq = dQ + row_id * kHeadDim;
+        const float scale = (!VARLEN || q < len) ? s : 0.0f;
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            f32x4 v0 = {dq0[4 * rg], dq0[4 * rg + 1], dq0[4 * rg + 2], dq0[4 * rg + 3]};
+            f32x4 v1 = {dq1[4 * rg], dq1[4 * rg + 1], dq1[4 * rg + 2], dq1[4 * rg + 3]};
+            *(f32x4*)(dq + 8 * rg + 4 * hi) = v0 * scale;
+            *(f32x4*)(dq + 32 + 8 * rg + 4 * hi) = v1 * scale;
+        }
+    };
+    process(items[0]);
+    if (n_items == 2) {
+        __syncthreads();  // every wave is past the first item's last tile reads
+        process(items[1]);
+    }
+}
+
+}  // namespace
+
+size_t query_pass_blocks(const Shape& sh) {
+    const size_t n_qtiles = (size_t)((sh.T + kQpRows - 1) / kQpRows);
+    return (sh.block_order == 0 ? (n_qtiles + 1) / 2 : n_qtiles) * sh.batch * sh.heads;
+}
+
+hipError_t launch_query_pass(const Shape& sh, const void* dO, const void* O, const float* L, const void* Q,
+                             const void* K, const void* Vt, float c, float s, float* D, float* dQ,
+                             hipStream_t stream) {
+    const int n_qtiles = (sh.T + kQpRows - 1) / kQpRows;
+    const int BH = sh.batch * sh.heads;
+    dim3 grid((unsigned)query_pass_blocks(sh)), block(kQpThreads);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, block, 0, stream, (const half_t*)Q, (const half_t*)K, (const half_t*)Vt,
+                           (const half_t*)dO, (const half_t*)O, L, D, dQ, sh.seqlens, c, s, sh.T, sh.heads,
+                           sh.kv_heads, n_qtiles, BH, sh.block_order);
+    };
+    const bool varlen = sh.seqlens != nullptr;
+    if (sh.causal) {
+        if (varlen) go(sa_query_kernel<true, true>);
+        else go(sa_query_kernel<true, false>);
+    } else {
+        if (varlen) go(sa_query_kernel<false, true>);
+        else go(sa_query_kernel<false, false>);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sa

@@ -152,7 +152,8 @@ sa_status sa_row_terms(const sa_shape* shape, const void* dO, const void* O, flo
  * gradients, per the split query pass's banner): for every 64-key tile,
  * recompute S, P and dP for every later query, accumulate dK and dV over the
  * group's heads and store dS (fp16, the words the dK product uses) into the
- * workspace, exact zeros where masked.
+ * workspace, exact zeros where masked.  dS may be NULL (dS_bytes is then
+ * ignored): nothing is stored, as in the two-launch backward's key launch.
  */
 sa_status sa_key_pass(const sa_shape* shape, const void* Q, const void* K, const void* Vt,
                       const void* dO, const float* L, const float* D, void* dS, size_t dS_bytes,
@@ -165,6 +166,34 @@ sa_status sa_key_pass(const sa_shape* shape, const void* Q, const void* K, const
  */
 sa_status sa_dq_pass(const sa_shape* shape, const void* K, const void* dS, size_t dS_bytes, float s,
                      float* dQ, void* stream);
+
+/*
+ * The backward in two launches, with no dS workspace (StreamingAttentionSM86
+ * page, banner "The backward pass, deterministic and in two launches (no
+ * atomics)"): the query launch forms D and dQ, recomputing S, P and dP per
+ * key tile; the key launch forms dK and dV the same way.  S, P and dP are
+ * formed twice instead of once, and nothing of size T x T is stored.
+ *
+ * Query pass: D = rowsum(dO * O) for every row (written, 0 on padded rows),
+ * and dQ = s * sum_j dS_ij K_j with dS = P (dP - D), P = 2^(S c - L),
+ * dP = dO V^T, walking the key tiles up to the diagonal.
+ *   dO, O, L: as sa_backward (O and L this shape's sa_forward outputs).
+ *   Q, K, Vt: the forward's inputs.  c, s: as sa_backward.
+ *   D, dQ: fp32 outputs, fully overwritten.
+ */
+sa_status sa_query_pass(const sa_shape* shape, const void* dO, const void* O, const float* L,
+                        const void* Q, const void* K, const void* Vt, float c, float s,
+                        float* D, float* dQ, void* stream);
+
+/*
+ * The two-launch backward: sa_query_pass, then the key pass without a dS
+ * store (dK, dV^T).  Arguments as sa_backward_ex without the workspace;
+ * results agree with it up to rounding (the score products are formed in
+ * another operand orientation).
+ */
+sa_status sa_backward_two_pass(const sa_shape* shape, const void* dO, const void* O, const float* L,
+                               float* D, const void* Q, const void* K, const void* Vt, float c, float s,
+                               float* dQ, float* dK, float* dVt, void* stream);
 
 /* Static text for a status value ("unknown status" for anything else). */
 const char* sa_status_string(int status);

@@ -23,13 +23,18 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_gpu(inputs, causal, block_order=0, backward=True):
-    """Forward (and backward) on cuda:0; returns the buffers object and numpy copies."""
+def run_gpu(inputs, causal, block_order=0, backward=True, path="split"):
+    """Forward (and backward) on cuda:0; returns the buffers object and numpy copies.
+    path "split" is the three-launch backward through the dS workspace,
+    "two_pass" the two-launch backward that stores no dS."""
     import torch
     buf = sa.Buffers(inputs, causal, block_order=block_order)
     buf.forward(C)
-    if backward:
+    if backward and path == "split":
         buf.backward(C, SCALE)
+    elif backward:
+        assert path == "two_pass", path
+        buf.backward_two_pass(C, SCALE)
     torch.cuda.synchronize()
     B, H, T = buf.B, buf.H, buf.T
     out = {

@@ -135,8 +135,48 @@ def test_stage_entry_points_reject_bad_arguments(lib):
     assert lib.sa_row_terms(ctypes.byref(s), FAKE, None, FAKE, None) == sa.SA_ERR_NULL
     assert lib.sa_key_pass(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 2, 0.18, 0.125,
                            FAKE, FAKE, None) == sa.SA_ERR_WORKSPACE
+    # dS may be NULL (no store): the workspace size is then not checked, the rest still is
+    assert lib.sa_key_pass(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 0.18, -0.125,
+                           FAKE, FAKE, None) == sa.SA_ERR_ARGUMENT
+    assert lib.sa_key_pass(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, 0.18, 0.125,
+                           FAKE, FAKE, None) == sa.SA_ERR_NULL
+    assert lib.sa_key_pass(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4, need, 0.18, 0.125,
+                           FAKE, FAKE, None) == sa.SA_ERR_ALIGN
     assert lib.sa_dq_pass(ctypes.byref(s), FAKE, FAKE, need, -0.125, FAKE, None) == sa.SA_ERR_ARGUMENT
     assert lib.sa_dq_pass(ctypes.byref(s), FAKE, FAKE + 1, need, 0.125, FAKE, None) == sa.SA_ERR_ALIGN
+
+
+def test_two_pass_entry_points_reject_bad_arguments(lib):
+    s = shape()
+    q_ptrs = [FAKE] * 8   # dO O L Q K Vt D dQ
+
+    def query(p, c=0.18, sc=0.125, sh=s):
+        return lib.sa_query_pass(ctypes.byref(sh), p[0], p[1], p[2], p[3], p[4], p[5], c, sc, p[6], p[7], None)
+
+    for i in range(8):
+        bad = list(q_ptrs)
+        bad[i] = None
+        assert query(bad) == sa.SA_ERR_NULL
+        bad[i] = FAKE + 2
+        assert query(bad) == sa.SA_ERR_ALIGN
+    assert query(q_ptrs, c=0.0) == sa.SA_ERR_ARGUMENT
+    assert query(q_ptrs, sc=float("inf")) == sa.SA_ERR_ARGUMENT
+    assert query(q_ptrs, sh=shape(T=100)) == sa.SA_ERR_SHAPE
+
+    b_ptrs = [FAKE] * 10  # dO O L D Q K Vt dQ dK dVt
+
+    def two_pass(p, c=0.18, sc=0.125, sh=s):
+        return lib.sa_backward_two_pass(ctypes.byref(sh), *p[:7], c, sc, *p[7:], None)
+
+    for i in range(10):
+        bad = list(b_ptrs)
+        bad[i] = None
+        assert two_pass(bad) == sa.SA_ERR_NULL
+        bad[i] = FAKE + 8
+        assert two_pass(bad) == sa.SA_ERR_ALIGN
+    assert two_pass(b_ptrs, sc=-1.0) == sa.SA_ERR_ARGUMENT
+    assert two_pass(b_ptrs, sh=shape(heads=6, kv=4)) == sa.SA_ERR_SHAPE
+    assert lib.sa_backward_two_pass(None, *b_ptrs[:7], 0.18, 0.125, *b_ptrs[7:], None) == sa.SA_ERR_NULL
 
 
 def test_status_strings(lib):

@@ -1,0 +1,134 @@
+"""GPU parity of the two-launch backward (query pass for D and dQ, then the
+key pass without a dS store), through the C ABI, against the binary64
+oracle: the same tolerances, cases and invariants as the three-launch path.
+Every test here needs an MI355X."""
+import numpy as np
+import pytest
+
+import oracle
+from causal_streaming_attention_amd.workloads import SCALE, WORKLOADS, generate, make_inputs
+from parity_util import (check_forward, check_grad, full_reference, rel_l2, run_gpu, sample_cols, sample_rows,
+                         say)
+from test_gpu_parity import SMALL, _gradient_sums
+
+pytestmark = pytest.mark.gpu
+PATH = "two_pass"
+
+
+def _check_all(inputs, causal, where):
+    _, got = run_gpu(inputs, causal, path=PATH)
+    ref = full_reference(inputs, causal)
+    check_forward(got["O"], got["L"], ref["O"], ref["L"], where)
+    errs = {k: check_grad(k, got[k], ref[k], where) for k in ("dQ", "dK", "dVt")}
+    if inputs["seqlens"] is not None:
+        for b, n in enumerate(inputs["seqlens"]):
+            assert np.all(got["D"][b, :, n:] == 0) and np.all(got["dQ"][b, :, n:] == 0), where
+            assert np.all(got["dK"][b, :, n:] == 0) and np.all(got["dVt"][b, :, :, n:] == 0), where
+    assert rel_l2(got["D"], ref["D"]) <= 1e-2, where
+    say(f"{where} (two-pass): dQ {errs['dQ']:.2e} dK {errs['dK']:.2e} dV {errs['dVt']:.2e}")
+    return got
+
+
+@pytest.mark.parametrize("name,B,T,H,KV,causal,seqlens", SMALL, ids=[c[0] for c in SMALL])
+def test_two_pass_small_full_parity(name, B, T, H, KV, causal, seqlens):
+    say(f"case two-pass {name}")
+    x = make_inputs(B, T, H, KV, seed=100 + T + H, seqlens=seqlens)
+    _check_all(x, causal, name)
+
+
+def test_two_pass_causal_mha_t1024_workload():
+    w = WORKLOADS["causal_mha_t1024"]
+    say(f"case two-pass {w.name}")
+    _check_all(generate(w), w.causal, w.name)
+
+
+def _sampled(w, n_rows, n_cols, kv_list, col_lo=0):
+    x = generate(w)
+    say(f"case two-pass {w.name}: gpu")
+    _, got = run_gpu(x, w.causal, path=PATH)
+    B, H, T, KV = w.batch, w.heads, w.T, w.kv_heads
+    rows = sample_rows(B, H, T, n_rows, seed=w.seed + 10)
+    say(f"case two-pass {w.name}: oracle rows {rows.size}")
+    D, dQ, O, L = oracle.backward_rows(x["Q"], x["K"], x["Vt"], x["dO"], s=SCALE, causal=w.causal,
+                                       seqlens=x["seqlens"], rows=rows)
+    check_forward(got["O"].reshape(-1, 64)[rows], got["L"].reshape(-1)[rows], O, L, w.name)
+    check_grad("dQ", got["dQ"].reshape(-1, 64)[rows], dQ, w.name)
+    assert rel_l2(got["D"].reshape(-1)[rows], D) <= 1e-2
+    cols = sample_cols(B, KV, T, n_cols, seed=w.seed + 11, kv_list=kv_list, lo=col_lo)
+    say(f"case two-pass {w.name}: oracle cols {cols.size}")
+    dK, dV = oracle.backward_cols(x["Q"], x["K"], x["Vt"], x["dO"], s=SCALE, causal=w.causal,
+                                  seqlens=x["seqlens"], cols=cols)
+    check_grad("dK", got["dK"].reshape(-1, 64)[cols], dK, w.name)
+    check_grad("dV", np.swapaxes(got["dVt"], -1, -2).reshape(-1, 64)[cols], dV, w.name)
+    return x, got
+
+
+def test_two_pass_causal_gqa_t4096_workload_sampled():
+    w = WORKLOADS["causal_gqa_t4096"]
+    x, got = _sampled(w, 384, 160, kv_list=[1, 6])
+    _gradient_sums(x, got, w)
+
+
+def test_two_pass_varlen_b16_t2048_workload_sampled():
+    w = WORKLOADS["varlen_b16_t2048"]
+    x, got = _sampled(w, 384, 128, kv_list=[9])
+    for b, n in enumerate(x["seqlens"]):
+        assert np.all(got["dQ"][b, :, n:] == 0) and np.all(got["D"][b, :, n:] == 0)
+        assert np.all(got["dK"][b, :, n:] == 0) and np.all(got["dVt"][b, :, :, n:] == 0)
+    _gradient_sums(x, got, w)
+
+
+def test_two_pass_agrees_with_the_split_backward():
+    """Both paths compute the same gradients; they differ only in rounding."""
+    w = WORKLOADS["causal_gqa_t4096"]
+    say("case two-pass vs split")
+    x = generate(w)
+    _, a = run_gpu(x, True, path="split")
+    _, b = run_gpu(x, True, path=PATH)
+    for k in ("dQ", "dK", "dVt"):
+        e = rel_l2(b[k], a[k])
+        say(f"  {k}: rel L2 {e:.2e}")
+        assert e <= 1e-2, k
+    assert rel_l2(b["D"], a["D"]) <= 1e-5
+
+
+def test_two_pass_determinism_and_block_order():
+    w = WORKLOADS["causal_gqa_t4096"]
+    say("case two-pass determinism")
+    x = generate(w)
+    _, a = run_gpu(x, True, block_order=0, path=PATH)
+    _, b = run_gpu(x, True, block_order=0, path=PATH)
+    _, c = run_gpu(x, True, block_order=1, path=PATH)
+    for k in a:
+        assert np.array_equal(a[k], b[k], equal_nan=True), f"{k} differs between repeats"
+        assert np.array_equal(a[k], c[k], equal_nan=True), f"{k} differs between block orders"
+
+
+def test_two_pass_padding_garbage_does_not_leak():
+    say("case two-pass padding-garbage")
+    lens = [100, 37, 192]
+    x = make_inputs(3, 192, 4, 2, seed=23, seqlens=lens)
+    for causal in (False, True):
+        _, clean = run_gpu(x, causal, path=PATH)
+        dirty = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in x.items()}
+        rng = np.random.default_rng(1)
+        for b, n in enumerate(lens):
+            for k in ("Q", "K", "dO"):
+                pad = dirty[k][b, :, n:]
+                pad[...] = rng.choice([-65504.0, 65504.0], size=pad.shape).astype(np.float16)
+            pad = dirty["Vt"][b, :, :, n:]
+            pad[...] = rng.choice([-65504.0, 65504.0], size=pad.shape).astype(np.float16)
+        _, got = run_gpu(dirty, causal, path=PATH)
+        for k in clean:
+            assert np.array_equal(clean[k], got[k]), (causal, k)
+
+
+def test_two_pass_row_terms_from_the_forward_output():
+    """The query pass's D is rowsum(dO * O) of the forward's own fp16 O."""
+    say("case two-pass row-terms")
+    x = make_inputs(2, 256, 4, 4, seed=24, seqlens=[256, 77])
+    buf, got = run_gpu(x, True, path=PATH)
+    O16 = buf.O.view(2, 256, 4, 64).permute(0, 2, 1, 3).float().cpu().numpy().astype(np.float64)
+    want = np.sum(x["dO"].astype(np.float64) * O16, axis=-1)
+    want[1, :, 77:] = 0.0
+    assert np.max(np.abs(got["D"] - want)) <= 1e-5 * max(1.0, np.max(np.abs(want)))
