@@ -306,8 +306,11 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
             half4 x2 = lds_read_tr_async(dsx + tr_offset(lane, 16, 24, 0, kDsxRow));
             half4 x3 = lds_read_tr_async(dsx + tr_offset(lane, 20, 28, 0, kDsxRow));
             lds_wait4(x0, x1, x2, x3);
-            *(half8*)dsp = cat(x0, x1);
-            *(half8*)(dsp + 512) = cat(x2, x3);
+            // Non-temporal: dS is written once and read once, by the dQ pass;
+            // streamed past L2 it neither evicts the Q/dO rows the walk reuses
+            // nor stalls the walk behind L2 write-backs.
+            __builtin_nontemporal_store(cat(x0, x1), (half8*)dsp);
+            __builtin_nontemporal_store(cat(x2, x3), (half8*)(dsp + 512));
         }
         const half8 pp0 = half8_from_words(wp[0], wp[1], wp[2], wp[3]);
         const half8 pp1 = half8_from_words(wp[4], wp[5], wp[6], wp[7]);
@@ -489,10 +492,10 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
                             (CAUSAL ? (size_t)qt_l * (qt_l + 1) / 2 : (size_t)qt_l * nt) * (kTile * kTile);
         auto load_s = [&](int kt, half8 (&dst)[4]) {
             const half_t* t_ = dSw + (size_t)min(kt, kt_last) * (kTile * kTile);
-            dst[0] = gload16_async(t_);
-            dst[1] = gload16_async(t_ + 512);
-            dst[2] = gload16_async(t_ + 1024);
-            dst[3] = gload16_async(t_ + 1536);
+            dst[0] = gload16_stream_async(t_);
+            dst[1] = gload16_stream_async(t_ + 512);
+            dst[2] = gload16_stream_async(t_ + 1024);
+            dst[3] = gload16_stream_async(t_ + 1536);
         };
         // Every step issues K's DMA then the dS loads, on every path, so a
         // wave's count of loads younger than any given one is fixed: the

@@ -129,12 +129,13 @@ __device__ __forceinline__ void lds_write8_async(half_t* p, uint2 v) {
     const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) half_t*)(p);
     asm volatile("ds_write_b64 %0, %1" : : "v"(addr), "v"(v) : "memory");
 }
-// A 16-byte global load the compiler does not track: the caller must wait for
-// it with an s_waitcnt vmcnt that ties the result (asm "+v"), counting every
-// vector memory instruction issued after it.
-__device__ __forceinline__ half8 gload16_async(const void* p) {
+// A 16-byte non-temporal global load (data streamed once) that the compiler
+// does not track: the caller must wait for it with an s_waitcnt vmcnt that
+// ties the result (asm "+v"), counting every vector memory instruction
+// issued after it.
+__device__ __forceinline__ half8 gload16_stream_async(const void* p) {
     half8 r;
-    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+    asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(r) : "v"(p) : "memory");
     return r;
 }
 // Wait for every outstanding LDS read of this wave; the operands are tied so
