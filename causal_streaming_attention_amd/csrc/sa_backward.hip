@@ -86,14 +86,12 @@ __global__ __launch_bounds__(kRowThreads) void sa_row_terms_kernel(const half_t*
 constexpr int kSubRows = 32;
 constexpr int kSubBytes = kSubRows * kHeadDim * 2;          // 4096
 constexpr int kItemBytes = 2 * kSubBytes + 2 * kSubRows * 4;  // Q, dO, L, D: 8448
-constexpr int kDsxRow = 36;                                   // halves: 32 queries + pad
-constexpr int kDsxBytes = 32 * kDsxRow * 2;                  // one wave's 32x32 dS block
-constexpr int kWaveBytes = 2 * kItemBytes + kDsxBytes;
+constexpr int kWaveBytes = 2 * kItemBytes;
 constexpr int kRedRow = 68;                                  // floats
 
 template <int GW>
 struct KeyLds {
-    static constexpr int stage = 2 * GW * kWaveBytes;        // per wave: two items and a dS block
+    static constexpr int stage = 2 * GW * kWaveBytes;        // per wave: two items
     static constexpr int red = GW * 64 * kRedRow * 4;
     static constexpr int vt = 64 * kLdsRow * 2;
     static constexpr int bytes = stage > red ? (stage > vt ? stage : vt) : (red > vt ? red : vt);
@@ -186,7 +184,6 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     f32x16 dkacc0 = zero16(), dkacc1 = zero16(), dvacc0 = zero16(), dvacc1 = zero16();
 
     char* const wstage = smem + wave * kWaveBytes;  // this wave's two item buffers
-    half_t* const dsx = (half_t*)(wstage + 2 * kItemBytes);  // and its dS block [key][query]
     const int dma_row = lane >> 3;                         // + 8 u
     // Direct loads of one item into buffer `buf`: 4 x 1 KB of Q rows, 4 x 1 KB
     // of dO rows (lane l of load u: row 8 u + l / 8, stored chunk l % 8 holding
@@ -283,34 +280,21 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
             wd[2 * rg] = pack_half2(g[0], g[1]);
             wd[2 * rg + 1] = pack_half2(g[2], g[3]);
         }
-        // dS to global: through this wave's LDS block [key][query], read back
-        // transposed so that lane l holds 8 consecutive keys of query l % 32,
-        // and stored as two fully coalesced 1 KB runs.
-        // (asm writes: the compiler would otherwise wait for the next item's
-        // direct-to-LDS loads, which it cannot tell apart from dsx, first.)
-        // Without a workspace (the two-launch backward's key launch) nothing
-        // is stored.
+        // dS to the workspace (when there is one): this wave's 32x32 block of
+        // the 64x64 tile is quadrant (query half sub % 2, key half khalf), and
+        // each lane stores its key's 16 queries as the accumulator holds them
+        // (two 16-byte words: its queries of rows 0..15, then of 16..31), so a
+        // wave writes two fully coalesced 1 KB runs.  The dQ pass turns them
+        // into its operand layout.  Non-temporal: dS is written once and read
+        // once; streamed past L2 it neither evicts the Q/dO rows the walk
+        // reuses nor stalls the walk behind L2 write-backs.
         if (store_ds) {
-            // This wave's 32x32 block of the 64x64 dS tile: quadrant (query
-            // half sub % 2, key half khalf), stored as [key octet 4][query 32]
-            // [8 keys].
             const int qt = sub >> 1;
             const size_t tile = CAUSAL ? (size_t)qt * (qt + 1) / 2 + kt : (size_t)qt * (T / kTile) + kt;
             half_t* dsp = dS + (((size_t)b * H + head) * (size_t)tiles_per_head + tile) * (kTile * kTile) +
                           (size_t)(2 * (sub & 1) + khalf) * 1024 + 8 * lane;
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg)
-                lds_write8_async(dsx + l32 * kDsxRow + 8 * rg + 4 * hi, make_uint2(wd[2 * rg], wd[2 * rg + 1]));
-            half4 x0 = lds_read_tr_async(dsx + tr_offset(lane, 0, 8, 0, kDsxRow));
-            half4 x1 = lds_read_tr_async(dsx + tr_offset(lane, 4, 12, 0, kDsxRow));
-            half4 x2 = lds_read_tr_async(dsx + tr_offset(lane, 16, 24, 0, kDsxRow));
-            half4 x3 = lds_read_tr_async(dsx + tr_offset(lane, 20, 28, 0, kDsxRow));
-            lds_wait4(x0, x1, x2, x3);
-            // Non-temporal: dS is written once and read once, by the dQ pass;
-            // streamed past L2 it neither evicts the Q/dO rows the walk reuses
-            // nor stalls the walk behind L2 write-backs.
-            __builtin_nontemporal_store(cat(x0, x1), (half8*)dsp);
-            __builtin_nontemporal_store(cat(x2, x3), (half8*)(dsp + 512));
+            __builtin_nontemporal_store(half8_from_words(wd[0], wd[1], wd[2], wd[3]), (half8*)dsp);
+            __builtin_nontemporal_store(half8_from_words(wd[4], wd[5], wd[6], wd[7]), (half8*)(dsp + 512));
         }
         const half8 pp0 = half8_from_words(wp[0], wp[1], wp[2], wp[3]);
         const half8 pp1 = half8_from_words(wp[4], wp[5], wp[6], wp[7]);
@@ -392,21 +376,24 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
 // ---------------------------------------------------------------------------
 // dQ pass.  One 256-thread workgroup per 128 queries of a query head (two dS
 // tile rows); wave w owns 32 queries.  For each key tile up to the diagonal
-// (the query pass's order) the K tile is staged in LDS for the four waves
-// (double-buffered, its global loads two tiles ahead) and each wave
-// accumulates
-//   dQ^T += K^T dS^T   (A = K^T by transposed LDS reads; B = dS^T straight
-//                       from the workspace: its quadrant layout puts the 8
-//                       keys a lane needs for one query in 16 contiguous
-//                       bytes, and a wave's loads in two 512-byte runs)
-// with the dS loads of the next three tiles in flight, since the pass streams
-// the workspace from memory.  Each lane ends with 4-float runs of one query's
-// dQ row: dQ = s * sum, stored with 16-byte writes.
+// (the query pass's order) the K tile is staged in LDS for the four waves and
+// each wave accumulates
+//   dQ^T += K^T dS^T   (A = K^T by transposed LDS reads; B = dS^T: the key
+//                       pass stores dS as its accumulators hold it, a lane's
+//                       16 queries of one key, so each wave loads its 4 KB
+//                       block of the tile as four coalesced 1 KB runs, writes
+//                       it to its own LDS copy and reads it back transposed,
+//                       8 keys of one query per lane)
+// with the dS and K loads of the next four tiles in flight, since the pass
+// streams the workspace from memory.  Each lane ends with 4-float runs of
+// one query's dQ row: dQ = s * sum, stored with 16-byte writes.
 // ---------------------------------------------------------------------------
 constexpr int kDqWaves = 4;
 constexpr int kDqRows = 32 * kDqWaves;
 constexpr int kDqThreads = 64 * kDqWaves;
 constexpr int kKTileHalves = kTile * kHeadDim;  // unpadded, chunk-swizzled
+constexpr int kDsRunHalves = 512 + 32;          // a 1 KB dS run plus a 64-byte pad between its halves
+constexpr int kDsBlockHalves = 4 * kDsRunHalves;
 
 // dS tiles in flight per wave: the pass streams dS once from HBM, and the
 // registers are the deepest buffer the chip has (five tiles are 80 VGPRs).
@@ -431,6 +418,7 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
                                                                int T, int H, int KV, int n_qblk, int BH,
                                                                int block_order, long long tiles_per_head) {
     __shared__ __attribute__((aligned(16))) half_t lds[kDqDepth][kKTileHalves];  // K tiles
+    __shared__ __attribute__((aligned(16))) half_t dsl[kDqWaves][kDsBlockHalves];  // each wave's dS block
 
     const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -467,6 +455,23 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
         dma16(src + dma_row1 * kHeadDim + dma_c1 * 8, (char*)&lds[buf][(16 * wave + 8) * kHeadDim]);
     };
     const int trr = (lane & 15) >> 2, trc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // dS block in LDS: run u (quadrant kh = u / 2, query half u % 2) at
+    // kDsRunHalves u; within a run, lane L's 16 bytes (key L % 32 of the
+    // quadrant, queries of its half with (q / 4) % 2 = L / 32) at 8 L, plus
+    // a 32-half pad for L >= 32.
+    const int ds_slot = 8 * lane + ((lane >> 5) << 5);
+    // Transposed read of k-step s4, keys +4 j (j = 0, 1): 16-lane group G
+    // (= lane / 16) covers queries 16 (G % 2) + 0..15 and keys 8 (G / 2) +
+    // 0..3 of the run's quadrant; its lane 4 row + cq names queries
+    // 16 (G % 2) + 4 cq + 0..3 of key row `row`, stored in the run of query
+    // half G % 2 at lane (cq % 2) 32 + key, word 4 (cq / 2).
+    int ds_tr0[2];
+    {
+        const int G = lane >> 4, p = lane & 15, row = p >> 2, cq = p & 3;
+        const int in_run = 8 * ((cq & 1) * 32 + 8 * (G >> 1) + row) + 32 * (cq & 1) + 4 * (cq >> 1);
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) ds_tr0[kh] = kDsRunHalves * (2 * kh + (G & 1)) + in_run;
+    }
 
     auto process = [&](const int qblk) {
         const int qt0 = 2 * qblk;
@@ -481,14 +486,15 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
         const int kt_end_w = wave_rows && qt_w < ntl ? (CAUSAL ? min(qt_w + 1, kt_end) : kt_end) : 0;
         const int kt_clamp = max(kt_end - 1, 0);
 
-        // This lane's dS words of tile (qt_w, kt): quadrant (qh, kh) at 1024 kh,
-        // key octet kc = 2 (s % 2) + hi at 256 kc, query l32 at 8 l32.  Loads
-        // are issued on every path (see below), so their tile is clamped into
-        // the workspace: row qt_l, key tiles up to kt_last.
+        // This wave's dS block of tile (qt_w, kt): the quadrants (qh, 0) and
+        // (qh, 1), 4 KB at 2048 qh, loaded as four coalesced 1 KB runs (lane l
+        // takes 16 bytes at 8 l of each).  Loads are issued on every path (see
+        // below), so their tile is clamped into the workspace: row qt_l, key
+        // tiles up to kt_last.
         const int qt_l = min(qt_w, nt - 1);
         const int kt_last = CAUSAL ? qt_l : nt - 1;
         const half_t* dSw = dS + ((size_t)b * H + h) * (size_t)tiles_per_head * (kTile * kTile) +
-                            (size_t)(2 * qh) * 1024 + (size_t)hi * 256 + 8 * l32 +
+                            (size_t)(2 * qh) * 1024 + 8 * lane +
                             (CAUSAL ? (size_t)qt_l * (qt_l + 1) / 2 : (size_t)qt_l * nt) * (kTile * kTile);
         auto load_s = [&](int kt, half8 (&dst)[4]) {
             const half_t* t_ = dSw + (size_t)min(kt, kt_last) * (kTile * kTile);
@@ -524,6 +530,19 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
                 // dS tile kt, issued four steps back: 24 loads are younger.
                 static_assert((kDqLead) * kDqVmPerStep == 24, "the s_waitcnt immediate below");
                 asm volatile("s_waitcnt vmcnt(24)" : "+v"(cur[0]), "+v"(cur[1]), "+v"(cur[2]), "+v"(cur[3]));
+                // The block goes through this wave's LDS copy (each 1 KB run
+                // padded by 64 bytes between its two 512-byte halves) and comes
+                // back transposed: lane (query l32, hi) gets the 8 keys of
+                // k-step s4, 16 s4 + 8 hi + 0..7, of its query.
+                half_t* dw = dsl[wave];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) lds_write16_async(dw + kDsRunHalves * u + ds_slot, cur[u]);
+                half4 g[8];
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    g[2 * s4] = lds_read_tr_async(dw + ds_tr0[s4 >> 1] + 128 * (s4 & 1));
+                    g[2 * s4 + 1] = lds_read_tr_async(dw + ds_tr0[s4 >> 1] + 128 * (s4 & 1) + 32);
+                }
                 const half_t* Ks = lds[kt % kDqDepth];
                 half4 t[16];
 #pragma unroll
@@ -540,6 +559,7 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
                 }
                 lds_wait(t[0], t[1], t[2], t[3], t[4], t[5], t[6], t[7]);
                 lds_wait(t[8], t[9], t[10], t[11], t[12], t[13], t[14], t[15]);
+                lds_wait(g[0], g[1], g[2], g[3], g[4], g[5], g[6], g[7]);
                 if (VARLEN && (kt + 1) * kTile > len) {
                     // Keys at or past the length: the DMA brought whatever
                     // the padding holds; their dS is zero, so zero K too.
@@ -555,8 +575,9 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
                 }
 #pragma unroll
                 for (int s4 = 0; s4 < 4; ++s4) {
-                    acc0 = mfma32(cat(t[4 * s4 + 0], t[4 * s4 + 1]), cur[s4], acc0);
-                    acc1 = mfma32(cat(t[4 * s4 + 2], t[4 * s4 + 3]), cur[s4], acc1);
+                    const half8 bs = cat(g[2 * s4], g[2 * s4 + 1]);
+                    acc0 = mfma32(cat(t[4 * s4 + 0], t[4 * s4 + 1]), bs, acc0);
+                    acc1 = mfma32(cat(t[4 * s4 + 2], t[4 * s4 + 3]), bs, acc1);
                 }
             }
             // K tile kt + 1 (and every older load) has landed in LDS; every

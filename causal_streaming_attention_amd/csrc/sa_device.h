@@ -129,6 +129,11 @@ __device__ __forceinline__ void lds_write8_async(half_t* p, uint2 v) {
     const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) half_t*)(p);
     asm volatile("ds_write_b64 %0, %1" : : "v"(addr), "v"(v) : "memory");
 }
+// A 16-byte LDS write the compiler does not see as one (as lds_write8_async).
+__device__ __forceinline__ void lds_write16_async(half_t* p, half8 v) {
+    const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) half_t*)(p);
+    asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
 // A 16-byte non-temporal global load (data streamed once) that the compiler
 // does not track: the caller must wait for it with an s_waitcnt vmcnt that
 // ties the result (asm "+v"), counting every vector memory instruction
