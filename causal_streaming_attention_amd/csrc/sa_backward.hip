@@ -107,6 +107,16 @@ __device__ __forceinline__ int swz(int row, int col) {
     return row * kHeadDim + (((col >> 3) ^ swz_key(row)) << 3) + (col & 7);
 }
 
+// Issue-order hint for one key-pass item: the previous item's 8 dV / dK
+// products spread through this item's vector work.
+#define SA_SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+#define SA_KEY_SLOT SA_SGB(0x008, 1); SA_SGB(0x002, 8)
+#define SA_KEY_INTERLEAVE()                                   \
+    do {                                                      \
+        SA_KEY_SLOT; SA_KEY_SLOT; SA_KEY_SLOT; SA_KEY_SLOT;   \
+        SA_KEY_SLOT; SA_KEY_SLOT; SA_KEY_SLOT; SA_KEY_SLOT;   \
+    } while (0)
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ void dma16(const void* g, char* lds_wave_base) {
@@ -211,11 +221,57 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     // them as possibly outstanding and drains every load before the products.
     vm_wait_all();
 
+    // Transposed reads of a staged item's dO^T and Q^T rows, the A operands of
+    // its dV^T += dO^T P and dK^T += Q^T dS products; k-step ks covers queries
+    // 16 ks + 4 hi + 0..3 and 16 ks + 8 + 4 hi + 0..3.  Transposed read: lane
+    // l gets column (16 ((l / 16) % 2) + l % 16) of rows row0 + 0..3.
+    const int trr = (lane & 15) >> 2, trc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    auto read_transposed = [&](const half_t* Qs, half4 (&t)[16]) {
+        const half_t* dOs = Qs + kSubRows * kHeadDim;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int ra = 16 * ks + 4 * hi + trr, rb = ra + 8;
+            t[8 * ks + 0] = lds_read_tr_async(dOs + swz(ra, trc));
+            t[8 * ks + 1] = lds_read_tr_async(dOs + swz(rb, trc));
+            t[8 * ks + 2] = lds_read_tr_async(dOs + swz(ra, 32 + trc));
+            t[8 * ks + 3] = lds_read_tr_async(dOs + swz(rb, 32 + trc));
+            t[8 * ks + 4] = lds_read_tr_async(Qs + swz(ra, trc));
+            t[8 * ks + 5] = lds_read_tr_async(Qs + swz(rb, trc));
+            t[8 * ks + 6] = lds_read_tr_async(Qs + swz(ra, 32 + trc));
+            t[8 * ks + 7] = lds_read_tr_async(Qs + swz(rb, 32 + trc));
+        }
+        lds_wait(t[0], t[1], t[2], t[3], t[4], t[5], t[6], t[7]);
+        lds_wait(t[8], t[9], t[10], t[11], t[12], t[13], t[14], t[15]);
+    };
+    auto accumulate = [&](const half4 (&t)[16], const uint32_t (&wp)[8], const uint32_t (&wd)[8]) {
+        const half8 pp0 = half8_from_words(wp[0], wp[1], wp[2], wp[3]);
+        const half8 pp1 = half8_from_words(wp[4], wp[5], wp[6], wp[7]);
+        const half8 pd0 = half8_from_words(wd[0], wd[1], wd[2], wd[3]);
+        const half8 pd1 = half8_from_words(wd[4], wd[5], wd[6], wd[7]);
+        dvacc0 = mfma32(cat(t[0], t[1]), pp0, dvacc0);
+        dvacc1 = mfma32(cat(t[2], t[3]), pp0, dvacc1);
+        dkacc0 = mfma32(cat(t[4], t[5]), pd0, dkacc0);
+        dkacc1 = mfma32(cat(t[6], t[7]), pd0, dkacc1);
+        dvacc0 = mfma32(cat(t[8], t[9]), pp1, dvacc0);
+        dvacc1 = mfma32(cat(t[10], t[11]), pp1, dvacc1);
+        dkacc0 = mfma32(cat(t[12], t[13]), pd1, dkacc0);
+        dkacc1 = mfma32(cat(t[14], t[15]), pd1, dkacc1);
+    };
+
+    // P and dS of the previous item, packed as binary16 pairs in accumulator
+    // order: the B operands of its dV and dK products, which run inside this
+    // item's vector work.  Before the first item they are zero and the first
+    // item's own (finite) rows stand in for the previous item's, so those
+    // products add exact zeros.
+    uint32_t wp[8], wd[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wp[i] = wd[i] = 0u;
+
     for (int it = 0; it < n_items; ++it) {
         const int buf = it & 1;
-        // This item's loads were issued at the top of the previous item, and
-        // only that item's two dS stores (if dS is stored) are younger: wait
-        // for the loads, not for the stores to reach memory.
+        // This item's loads were issued in the previous item, and only that
+        // item's two dS stores (if dS is stored) are younger: wait for the
+        // loads, not for the stores to reach memory.
         if (store_ds) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         int next_head = head, next_sub = sub - 1;
@@ -241,6 +297,10 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
             }
             if ((lane & 31) >= keep) Ls[lane] = 0.0f;  // L (lanes 0..31) and D (32..63)
         }
+        // The previous item's transposed operands; once they are in registers
+        // its buffer takes the next item.
+        half4 t[16];
+        read_transposed((const half_t*)(wstage + (it == 0 ? buf : buf ^ 1) * kItemBytes), t);
         if (it + 1 < n_items) issue_item(next_head, next_sub, buf ^ 1);
 
         // A block with no admitted pair (the diagonal sub-tile of the upper key
@@ -248,37 +308,40 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
         // dS exact zeros.
         f32x16 sacc = zero16(), pacc = zero16();
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const int off = swz(l32, 16 * q4 + 8 * hi);
-            sacc = mfma32(*(const half8*)(Qs + off), kf[q4], sacc);
-            pacc = mfma32(*(const half8*)(dOs + off), vf[q4], pacc);
-        }
-        const bool need_mask = (CAUSAL && qb < kbase + 31) || (VARLEN && (qb + kSubRows > len || kbase + 32 > len));
-        uint32_t wp[8], wd[8];  // P and dS packed as binary16 pairs, accumulator order
+        for (int q4 = 0; q4 < 4; ++q4) sacc = mfma32(*(const half8*)(Qs + swz(l32, 16 * q4 + 8 * hi)), kf[q4], sacc);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) pacc = mfma32(*(const half8*)(dOs + swz(l32, 16 * q4 + 8 * hi)), vf[q4], pacc);
+        f32x4 lv[4], dv[4];
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-            const f32x4 lv = *(const f32x4*)(Ls + 8 * rg + 4 * hi);
-            const f32x4 dv = *(const f32x4*)(Ds + 8 * rg + 4 * hi);
-            float p[4], g[4];
+            lv[rg] = *(const f32x4*)(Ls + 8 * rg + 4 * hi);
+            dv[rg] = *(const f32x4*)(Ds + 8 * rg + 4 * hi);
+        }
+        // The previous item's products go into the matrix pipe behind these,
+        // one between every few of this item's vector instructions.
+        __builtin_amdgcn_sched_barrier(0);
+        accumulate(t, wp, wd);
+        float p[16], g[16];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * rg + e;
-                p[e] = exp2_fast(__builtin_fmaf(sacc[r], c, -lv[e]));
-                g[e] = p[e] * (pacc[r] - dv[e]);
-            }
-            if (need_mask) {
+        for (int r = 0; r < 16; ++r) {
+            p[r] = exp2_fast(__builtin_fmaf(sacc[r], c, -lv[r >> 2][r & 3]));
+            g[r] = p[r] * (pacc[r] - dv[r >> 2][r & 3]);
+        }
+        SA_KEY_INTERLEAVE();
+        const bool need_mask = (CAUSAL && qb < kbase + 31) || (VARLEN && (qb + kSubRows > len || kbase + 32 > len));
+        if (need_mask) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int q = qb + 8 * rg + 4 * hi + e;
-                    const bool masked = (CAUSAL && key > q) || (VARLEN && (q >= len || key >= len));
-                    p[e] = masked ? 0.0f : p[e];
-                    g[e] = masked ? 0.0f : g[e];
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int q = qb + 8 * (r >> 2) + 4 * hi + (r & 3);
+                const bool masked = (CAUSAL && key > q) || (VARLEN && (q >= len || key >= len));
+                p[r] = masked ? 0.0f : p[r];
+                g[r] = masked ? 0.0f : g[r];
             }
-            wp[2 * rg] = pack_half2(p[0], p[1]);
-            wp[2 * rg + 1] = pack_half2(p[2], p[3]);
-            wd[2 * rg] = pack_half2(g[0], g[1]);
-            wd[2 * rg + 1] = pack_half2(g[2], g[3]);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            wp[i] = pack_half2(p[2 * i], p[2 * i + 1]);
+            wd[i] = pack_half2(g[2 * i], g[2 * i + 1]);
         }
         // dS to the workspace (when there is one): this wave's 32x32 block of
         // the 64x64 tile is quadrant (query half sub % 2, key half khalf), and
@@ -296,39 +359,14 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
             __builtin_nontemporal_store(half8_from_words(wd[0], wd[1], wd[2], wd[3]), (half8*)dsp);
             __builtin_nontemporal_store(half8_from_words(wd[4], wd[5], wd[6], wd[7]), (half8*)(dsp + 512));
         }
-        const half8 pp0 = half8_from_words(wp[0], wp[1], wp[2], wp[3]);
-        const half8 pp1 = half8_from_words(wp[4], wp[5], wp[6], wp[7]);
-        const half8 pd0 = half8_from_words(wd[0], wd[1], wd[2], wd[3]);
-        const half8 pd1 = half8_from_words(wd[4], wd[5], wd[6], wd[7]);
-        // dV^T += dO^T P and dK^T += Q^T dS; k-step ks covers queries
-        // 16 ks + 4 hi + 0..3 and 16 ks + 8 + 4 hi + 0..3.  Transposed read:
-        // lane l gets column (16 ((l / 16) % 2) + l % 16) of rows row0 + 0..3.
-        const int trr = (lane & 15) >> 2, trc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        half4 t[16];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int ra = 16 * ks + 4 * hi + trr, rb = ra + 8;
-            t[8 * ks + 0] = lds_read_tr_async(dOs + swz(ra, trc));
-            t[8 * ks + 1] = lds_read_tr_async(dOs + swz(rb, trc));
-            t[8 * ks + 2] = lds_read_tr_async(dOs + swz(ra, 32 + trc));
-            t[8 * ks + 3] = lds_read_tr_async(dOs + swz(rb, 32 + trc));
-            t[8 * ks + 4] = lds_read_tr_async(Qs + swz(ra, trc));
-            t[8 * ks + 5] = lds_read_tr_async(Qs + swz(rb, trc));
-            t[8 * ks + 6] = lds_read_tr_async(Qs + swz(ra, 32 + trc));
-            t[8 * ks + 7] = lds_read_tr_async(Qs + swz(rb, 32 + trc));
-        }
-        lds_wait(t[0], t[1], t[2], t[3], t[4], t[5], t[6], t[7]);
-        lds_wait(t[8], t[9], t[10], t[11], t[12], t[13], t[14], t[15]);
-        dvacc0 = mfma32(cat(t[0], t[1]), pp0, dvacc0);
-        dvacc1 = mfma32(cat(t[2], t[3]), pp0, dvacc1);
-        dkacc0 = mfma32(cat(t[4], t[5]), pd0, dkacc0);
-        dkacc1 = mfma32(cat(t[6], t[7]), pd0, dkacc1);
-        dvacc0 = mfma32(cat(t[8], t[9]), pp1, dvacc0);
-        dvacc1 = mfma32(cat(t[10], t[11]), pp1, dvacc1);
-        dkacc0 = mfma32(cat(t[12], t[13]), pd1, dkacc0);
-        dkacc1 = mfma32(cat(t[14], t[15]), pd1, dkacc1);
         head = next_head;
         sub = next_sub;
+    }
+    // The last item's products.
+    if (n_items > 0) {
+        half4 t[16];
+        read_transposed((const half_t*)(wstage + ((n_items - 1) & 1) * kItemBytes), t);
+        accumulate(t, wp, wd);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // every wave is done with its staging buffers
