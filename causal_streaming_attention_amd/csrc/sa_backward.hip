@@ -122,6 +122,13 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void dma16(const void* g, char* lds_wave_base) {
     __builtin_amdgcn_global_load_lds(g, (lds_void*)((__attribute__((address_space(3))) char*)lds_wave_base), 16, 0, 0);
 }
+// 16-byte direct load at g + OFF into LDS at lds_wave_base + OFF + 16 lane:
+// the offset field moves both addresses.
+template <int OFF>
+__device__ __forceinline__ void dma16_at(const void* g, char* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)((__attribute__((address_space(3))) char*)lds_wave_base), 16, OFF,
+                                     0);
+}
 __device__ __forceinline__ void dma4(const void* g, char* lds_wave_base) {
     __builtin_amdgcn_global_load_lds(g, (lds_void*)((__attribute__((address_space(3))) char*)lds_wave_base), 4, 0, 0);
 }
@@ -198,17 +205,22 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     // Direct loads of one item into buffer `buf`: 4 x 1 KB of Q rows, 4 x 1 KB
     // of dO rows (lane l of load u: row 8 u + l / 8, stored chunk l % 8 holding
     // the row's chunk (l % 8) ^ swz_key(row)), then L (lanes 0..31) and D (32..63).
+    // Row 8 u + r has the chunk permutation of row r, so load u is load 0
+    // moved by 1 KB in memory and in LDS: the instruction's offset field.
+    const uint32_t dma_off = (uint32_t)(dma_row * kHeadDim + ((lane & 7) ^ swz_key(dma_row)) * 8) * 2u;
     auto issue_item = [&](int head, int sub, int buf) {
         const size_t rowbase = ((size_t)b * H + head) * T + (size_t)sub * kSubRows;
+        const char* qg = (const char*)(Q + rowbase * kHeadDim) + dma_off;
+        const char* og = (const char*)(dO + rowbase * kHeadDim) + dma_off;
         char* base = wstage + buf * kItemBytes;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int row = 8 * u + dma_row;
-            const int col = ((lane & 7) ^ swz_key(row)) * 8;
-            const size_t off = (rowbase + row) * kHeadDim + col;
-            dma16(Q + off, base + 1024 * u);
-            dma16(dO + off, base + kSubBytes + 1024 * u);
-        }
+        dma16_at<0>(qg, base);
+        dma16_at<1024>(qg, base);
+        dma16_at<2048>(qg, base);
+        dma16_at<3072>(qg, base);
+        dma16_at<0>(og, base + kSubBytes);
+        dma16_at<1024>(og, base + kSubBytes);
+        dma16_at<2048>(og, base + kSubBytes);
+        dma16_at<3072>(og, base + kSubBytes);
         const float* src = (lane < 32) ? (L + rowbase + lane) : (D + rowbase + (lane - 32));
         dma4(src, base + 2 * kSubBytes);
     };
@@ -225,21 +237,29 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     // its dV^T += dO^T P and dK^T += Q^T dS products; k-step ks covers queries
     // 16 ks + 4 hi + 0..3 and 16 ks + 8 + 4 hi + 0..3.  Transposed read: lane
     // l gets column (16 ((l / 16) % 2) + l % 16) of rows row0 + 0..3.
+    // Rows r + 8 and r + 16 have row r's chunk permutation, so of the 16
+    // reads only the column halves (d 0..31 and 32..63) need their own lane
+    // addresses; rows, k-steps and Q versus dO are offsets of 1, 2 and 4 KB.
     const int trr = (lane & 15) >> 2, trc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const uint32_t tr_c0 = (uint32_t)swz(4 * hi + trr, trc) * 2u, tr_c1 = (uint32_t)swz(4 * hi + trr, 32 + trc) * 2u;
     auto read_transposed = [&](const half_t* Qs, half4 (&t)[16]) {
-        const half_t* dOs = Qs + kSubRows * kHeadDim;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int ra = 16 * ks + 4 * hi + trr, rb = ra + 8;
-            t[8 * ks + 0] = lds_read_tr_async(dOs + swz(ra, trc));
-            t[8 * ks + 1] = lds_read_tr_async(dOs + swz(rb, trc));
-            t[8 * ks + 2] = lds_read_tr_async(dOs + swz(ra, 32 + trc));
-            t[8 * ks + 3] = lds_read_tr_async(dOs + swz(rb, 32 + trc));
-            t[8 * ks + 4] = lds_read_tr_async(Qs + swz(ra, trc));
-            t[8 * ks + 5] = lds_read_tr_async(Qs + swz(rb, trc));
-            t[8 * ks + 6] = lds_read_tr_async(Qs + swz(ra, 32 + trc));
-            t[8 * ks + 7] = lds_read_tr_async(Qs + swz(rb, 32 + trc));
-        }
+        const uint32_t a0 = lds_addr(Qs) + tr_c0, a1 = lds_addr(Qs) + tr_c1;
+        t[0] = lds_read_tr_at<kSubBytes>(a0);
+        t[1] = lds_read_tr_at<kSubBytes + 1024>(a0);
+        t[2] = lds_read_tr_at<kSubBytes>(a1);
+        t[3] = lds_read_tr_at<kSubBytes + 1024>(a1);
+        t[4] = lds_read_tr_at<0>(a0);
+        t[5] = lds_read_tr_at<1024>(a0);
+        t[6] = lds_read_tr_at<0>(a1);
+        t[7] = lds_read_tr_at<1024>(a1);
+        t[8] = lds_read_tr_at<kSubBytes + 2048>(a0);
+        t[9] = lds_read_tr_at<kSubBytes + 3072>(a0);
+        t[10] = lds_read_tr_at<kSubBytes + 2048>(a1);
+        t[11] = lds_read_tr_at<kSubBytes + 3072>(a1);
+        t[12] = lds_read_tr_at<2048>(a0);
+        t[13] = lds_read_tr_at<3072>(a0);
+        t[14] = lds_read_tr_at<2048>(a1);
+        t[15] = lds_read_tr_at<3072>(a1);
         lds_wait(t[0], t[1], t[2], t[3], t[4], t[5], t[6], t[7]);
         lds_wait(t[8], t[9], t[10], t[11], t[12], t[13], t[14], t[15]);
     };

@@ -123,6 +123,19 @@ __device__ __forceinline__ half4 lds_read_tr_async(const half_t* p) {
     asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
     return r;
 }
+// The same read at LDS byte address addr + OFF, the constant part of the
+// address in the instruction's offset field.
+template <int OFF>
+__device__ __forceinline__ half4 lds_read_tr_at(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "DS offset field is 16 bits");
+    half4 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+    return r;
+}
+// LDS byte address of an element pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(p);
+}
 // An 8-byte LDS write the compiler does not see as one (no waits are placed
 // for it); a later asm LDS read and its lgkmcnt wait order after it.
 __device__ __forceinline__ void lds_write8_async(half_t* p, uint2 v) {
