@@ -97,11 +97,18 @@ struct KeyLds {
     static constexpr int bytes = stage > red ? (stage > vt ? stage : vt) : (red > vt ? red : vt);
 };
 
-// The chunk permutation of a staged sub-tile's row: f(r) is distinct for any 8
-// consecutive rows (a 16-byte read by 8 lanes of 8 rows) and f(r) / 2 is
-// distinct within each aligned group of 4 rows (a transposed read of 4 rows x
-// 2 chunks), so neither read pattern meets a bank conflict.
-__device__ __forceinline__ int swz_key(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// The chunk permutation of a staged sub-tile's row: LDS moves 256 bytes (64
+// banks) a cycle, two 128-byte rows side by side, so a 16-byte row read by 16
+// lanes (16 consecutive rows, one chunk) is free of bank conflicts when f(r)
+// is distinct over the 8 rows of each parity among them: f takes bits 1..3 of
+// r.  A transposed read covers 4 rows x 2 chunks of an aligned group of 4
+// rows, in which the two rows of a parity must land in different 4-chunk
+// halves: bit 2 of f(r) is bit 1 of r.
+__device__ __forceinline__ int swz_key(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
+// The dQ pass's K tiles are only read transposed: a key that depends on the
+// row's low three bits suffices (rows r and r + 2 of an aligned group of 4 in
+// different 4-chunk halves), and keeps that kernel's addressing cheap.
+__device__ __forceinline__ int swz_key_k(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 // Element offset of (row, col) in a swizzled 32 x 64 sub-tile.
 __device__ __forceinline__ int swz(int row, int col) {
     return row * kHeadDim + (((col >> 3) ^ swz_key(row)) << 3) + (col & 7);
@@ -205,22 +212,23 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     // Direct loads of one item into buffer `buf`: 4 x 1 KB of Q rows, 4 x 1 KB
     // of dO rows (lane l of load u: row 8 u + l / 8, stored chunk l % 8 holding
     // the row's chunk (l % 8) ^ swz_key(row)), then L (lanes 0..31) and D (32..63).
-    // Row 8 u + r has the chunk permutation of row r, so load u is load 0
-    // moved by 1 KB in memory and in LDS: the instruction's offset field.
-    const uint32_t dma_off = (uint32_t)(dma_row * kHeadDim + ((lane & 7) ^ swz_key(dma_row)) * 8) * 2u;
+    // Row 16 u + r has the chunk permutation of row r, so loads u and u + 2
+    // differ by 2 KB in memory and in LDS: the instruction's offset field.
+    const uint32_t dma_off0 = (uint32_t)(dma_row * kHeadDim + ((lane & 7) ^ swz_key(dma_row)) * 8) * 2u;
+    const uint32_t dma_off1 = (uint32_t)(dma_row * kHeadDim + ((lane & 7) ^ swz_key(dma_row + 8)) * 8) * 2u;
     auto issue_item = [&](int head, int sub, int buf) {
         const size_t rowbase = ((size_t)b * H + head) * T + (size_t)sub * kSubRows;
-        const char* qg = (const char*)(Q + rowbase * kHeadDim) + dma_off;
-        const char* og = (const char*)(dO + rowbase * kHeadDim) + dma_off;
+        const char* qrows = (const char*)(Q + rowbase * kHeadDim);
+        const char* orows = (const char*)(dO + rowbase * kHeadDim);
         char* base = wstage + buf * kItemBytes;
-        dma16_at<0>(qg, base);
-        dma16_at<1024>(qg, base);
-        dma16_at<2048>(qg, base);
-        dma16_at<3072>(qg, base);
-        dma16_at<0>(og, base + kSubBytes);
-        dma16_at<1024>(og, base + kSubBytes);
-        dma16_at<2048>(og, base + kSubBytes);
-        dma16_at<3072>(og, base + kSubBytes);
+        dma16_at<0>(qrows + dma_off0, base);
+        dma16_at<1024>(qrows + dma_off1, base);
+        dma16_at<2048>(qrows + dma_off0, base);
+        dma16_at<3072>(qrows + dma_off1, base);
+        dma16_at<0>(orows + dma_off0, base + kSubBytes);
+        dma16_at<1024>(orows + dma_off1, base + kSubBytes);
+        dma16_at<2048>(orows + dma_off0, base + kSubBytes);
+        dma16_at<3072>(orows + dma_off1, base + kSubBytes);
         const float* src = (lane < 32) ? (L + rowbase + lane) : (D + rowbase + (lane - 32));
         dma4(src, base + 2 * kSubBytes);
     };
@@ -237,29 +245,32 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     // its dV^T += dO^T P and dK^T += Q^T dS products; k-step ks covers queries
     // 16 ks + 4 hi + 0..3 and 16 ks + 8 + 4 hi + 0..3.  Transposed read: lane
     // l gets column (16 ((l / 16) % 2) + l % 16) of rows row0 + 0..3.
-    // Rows r + 8 and r + 16 have row r's chunk permutation, so of the 16
-    // reads only the column halves (d 0..31 and 32..63) need their own lane
-    // addresses; rows, k-steps and Q versus dO are offsets of 1, 2 and 4 KB.
+    // Row r + 16 has row r's chunk permutation, so of the 16 reads only the
+    // rows r and r + 8 and the column halves (d 0..31 and 32..63) need their
+    // own lane addresses; k-steps and Q versus dO are offsets of 2 and 4 KB.
     const int trr = (lane & 15) >> 2, trc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const uint32_t tr_c0 = (uint32_t)swz(4 * hi + trr, trc) * 2u, tr_c1 = (uint32_t)swz(4 * hi + trr, 32 + trc) * 2u;
+    const int tr_row = 4 * hi + trr;
+    const uint32_t tr_a0 = (uint32_t)swz(tr_row, trc) * 2u, tr_a1 = (uint32_t)swz(tr_row, 32 + trc) * 2u;
+    const uint32_t tr_b0 = (uint32_t)swz(tr_row + 8, trc) * 2u, tr_b1 = (uint32_t)swz(tr_row + 8, 32 + trc) * 2u;
     auto read_transposed = [&](const half_t* Qs, half4 (&t)[16]) {
-        const uint32_t a0 = lds_addr(Qs) + tr_c0, a1 = lds_addr(Qs) + tr_c1;
+        const uint32_t q = lds_addr(Qs);
+        const uint32_t a0 = q + tr_a0, a1 = q + tr_a1, b0 = q + tr_b0, b1 = q + tr_b1;
         t[0] = lds_read_tr_at<kSubBytes>(a0);
-        t[1] = lds_read_tr_at<kSubBytes + 1024>(a0);
+        t[1] = lds_read_tr_at<kSubBytes>(b0);
         t[2] = lds_read_tr_at<kSubBytes>(a1);
-        t[3] = lds_read_tr_at<kSubBytes + 1024>(a1);
+        t[3] = lds_read_tr_at<kSubBytes>(b1);
         t[4] = lds_read_tr_at<0>(a0);
-        t[5] = lds_read_tr_at<1024>(a0);
+        t[5] = lds_read_tr_at<0>(b0);
         t[6] = lds_read_tr_at<0>(a1);
-        t[7] = lds_read_tr_at<1024>(a1);
+        t[7] = lds_read_tr_at<0>(b1);
         t[8] = lds_read_tr_at<kSubBytes + 2048>(a0);
-        t[9] = lds_read_tr_at<kSubBytes + 3072>(a0);
+        t[9] = lds_read_tr_at<kSubBytes + 2048>(b0);
         t[10] = lds_read_tr_at<kSubBytes + 2048>(a1);
-        t[11] = lds_read_tr_at<kSubBytes + 3072>(a1);
+        t[11] = lds_read_tr_at<kSubBytes + 2048>(b1);
         t[12] = lds_read_tr_at<2048>(a0);
-        t[13] = lds_read_tr_at<3072>(a0);
+        t[13] = lds_read_tr_at<2048>(b0);
         t[14] = lds_read_tr_at<2048>(a1);
-        t[15] = lds_read_tr_at<3072>(a1);
+        t[15] = lds_read_tr_at<2048>(b1);
         lds_wait(t[0], t[1], t[2], t[3], t[4], t[5], t[6], t[7]);
         lds_wait(t[8], t[9], t[10], t[11], t[12], t[13], t[14], t[15]);
     };
@@ -503,10 +514,10 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
 
     // K DMA: wave w moves rows 8 (2 w + u) + lane / 8 (u = 0, 1) of a tile; a
     // lane's 16 bytes land at slot lane % 8 of its row, so it fetches the
-    // row's chunk (lane % 8) ^ swz_key(row): LDS holds chunk c of a row at
-    // c ^ swz_key(row).
+    // row's chunk (lane % 8) ^ swz_key_k(row): LDS holds chunk c of a row at
+    // c ^ swz_key_k(row).
     const int dma_row0 = 16 * wave + (lane >> 3), dma_row1 = dma_row0 + 8;
-    const int dma_c0 = (lane & 7) ^ swz_key(dma_row0), dma_c1 = (lane & 7) ^ swz_key(dma_row1);
+    const int dma_c0 = (lane & 7) ^ swz_key_k(dma_row0), dma_c1 = (lane & 7) ^ swz_key_k(dma_row1);
     auto dma_k = [&](int kt, int buf) {
         const half_t* src = Kp + (size_t)(kt * kTile) * kHeadDim;
         dma16(src + dma_row0 * kHeadDim + dma_c0 * 8, (char*)&lds[buf][(16 * wave) * kHeadDim]);
@@ -607,13 +618,13 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
                 for (int s4 = 0; s4 < 4; ++s4) {
                     // A = K^T: lane (d, hi) holds K[16 s4 + 8 hi + 0..7][d].
                     const int r0 = 16 * s4 + 8 * hi + trr;
-                    t[4 * s4 + 0] = lds_read_tr_async(Ks + r0 * kHeadDim + (((trc >> 3) ^ swz_key(r0)) << 3) + (trc & 7));
+                    t[4 * s4 + 0] = lds_read_tr_async(Ks + r0 * kHeadDim + (((trc >> 3) ^ swz_key_k(r0)) << 3) + (trc & 7));
                     t[4 * s4 + 1] = lds_read_tr_async(Ks + (r0 + 4) * kHeadDim +
-                                                      (((trc >> 3) ^ swz_key(r0 + 4)) << 3) + (trc & 7));
+                                                      (((trc >> 3) ^ swz_key_k(r0 + 4)) << 3) + (trc & 7));
                     t[4 * s4 + 2] = lds_read_tr_async(Ks + r0 * kHeadDim +
-                                                      ((((trc + 32) >> 3) ^ swz_key(r0)) << 3) + (trc & 7));
+                                                      ((((trc + 32) >> 3) ^ swz_key_k(r0)) << 3) + (trc & 7));
                     t[4 * s4 + 3] = lds_read_tr_async(Ks + (r0 + 4) * kHeadDim +
-                                                      ((((trc + 32) >> 3) ^ swz_key(r0 + 4)) << 3) + (trc & 7));
+                                                      ((((trc + 32) >> 3) ^ swz_key_k(r0 + 4)) << 3) + (trc & 7));
                 }
                 lds_wait(t[0], t[1], t[2], t[3], t[4], t[5], t[6], t[7]);
                 lds_wait(t[8], t[9], t[10], t[11], t[12], t[13], t[14], t[15]);

@@ -36,11 +36,14 @@ constexpr int kQpRows = 32 * kQpWaves;       // queries per workgroup
 constexpr int kQpThreads = 64 * kQpWaves;
 constexpr int kQpTile = kTile * kHeadDim;    // one unpadded 64x64 tile
 
-// Row r's 16-byte chunk c of a staged tile sits at chunk c ^ key(r): key is
-// distinct over any 8 consecutive rows (16-byte row reads by 8 lanes) and
-// key / 2 is distinct within each aligned group of 4 rows (a transposed read
-// of 4 rows x 2 chunks).
-__device__ __forceinline__ int qp_key(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// Row r's 16-byte chunk c of a staged tile sits at chunk c ^ key(r).  LDS
+// moves 256 bytes (64 banks) a cycle, two 128-byte rows side by side: a
+// 16-byte row read by 16 lanes (16 consecutive rows, one chunk) meets no bank
+// conflict when key is distinct over the 8 rows of each parity among them
+// (key takes bits 1..3 of r), and a transposed read of 4 rows x 2 chunks of
+// an aligned group of 4 rows none when the two rows of a parity land in
+// different 4-chunk halves (bit 2 of key is bit 1 of r).
+__device__ __forceinline__ int qp_key(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
 __device__ __forceinline__ int qp_swz(int row, int col) {
     return row * kHeadDim + (((col >> 3) ^ qp_key(row)) << 3) + (col & 7);
 }
