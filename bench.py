@@ -205,9 +205,9 @@ def main():
     ap.add_argument("--workload", default="causal_gqa_t4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--block-order", type=int, default=0)
-    ap.add_argument("--no-two-pass", action="store_true",
-                    help="skip the two-launch backward beside the timed path (profiles then see only the "
-                         "three-launch kernels)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the two-launch backward and the V-as-rows run timed beside the headline path "
+                         "(profiles then see only the headline's kernels)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="after the timed steps, run one device copy of this many MiB (the reference dispatch "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -297,8 +297,8 @@ def main():
                        stream)
         if ev: ev[3].record(stream)
 
-    two_pass = None
-    if not args.no_two_pass:
+    two_pass = v_rows = None
+    if not args.headline_only:
         for _ in range(args.warmup):
             step2()
         events2 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -315,6 +315,38 @@ def main():
                     "kernels_ms": {n: round(per2[n], 4) for n in names2},
                     "note": "same workload and FLOP convention; the backward recomputes S, P, dP in both passes "
                             "and stores no dS"}
+
+        # The headline path with V passed as rows [KV][T][64] (and dV returned so).
+        bufr = sa.Buffers(x, w.causal, block_order=args.block_order, v_rows=True)
+        shr = bufr.shape
+
+        def step3(ev=None):
+            if ev: ev[0].record(stream)
+            sa.sa_forward_ex(shr, bufr.Q, bufr.K, bufr.Vt, bufr.O, bufr.L, c, stream)
+            if ev: ev[1].record(stream)
+            sa.sa_row_terms(shr, bufr.dO, bufr.O, bufr.D, stream)
+            if ev: ev[2].record(stream)
+            sa.sa_key_pass(shr, bufr.Q, bufr.K, bufr.Vt, bufr.dO, bufr.L, bufr.D, bufr.dS, bufr.ws_bytes, c, SCALE,
+                           bufr.dK, bufr.dVt, stream)
+            if ev: ev[3].record(stream)
+            sa.sa_dq_pass(shr, bufr.K, bufr.dS, bufr.ws_bytes, SCALE, bufr.dQ, stream)
+            if ev: ev[4].record(stream)
+
+        for _ in range(args.warmup):
+            step3()
+        events3 = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for k in range(args.steps):
+            step3(events3[k])
+        torch.cuda.synchronize()
+        per3 = {n: float(np.mean([events3[k][i].elapsed_time(events3[k][i + 1]) for k in range(args.steps)]))
+                for i, n in enumerate(names)}
+        step3_ms = float(np.mean([events3[k][0].elapsed_time(events3[k][4]) for k in range(args.steps)]))
+        v_rows = {"ms_per_step": round(step3_ms, 4),
+                  "tflops": round(fl["total"] / (step3_ms * 1e-3) / 1e12, 2),
+                  "kernels_ms": {n: round(per3[n], 4) for n in names},
+                  "note": "the same step with V as rows [KV][T][64] (no transposed copy of V) and dV returned "
+                          "as rows; bitwise-identical outputs"}
 
     if args.calibrate_copy_mb > 0:
         n = args.calibrate_copy_mb << 20
@@ -337,6 +369,8 @@ def main():
     }
     if two_pass is not None:
         out["two_pass_backward"] = two_pass
+    if v_rows is not None:
+        out["v_rows"] = v_rows
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x)
     print(json.dumps(out), flush=True)

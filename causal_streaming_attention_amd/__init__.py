@@ -22,14 +22,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsa.so")
 _lib = None
 
-SA_OK, SA_ERR_SHAPE, SA_ERR_NULL, SA_ERR_ALIGN, SA_ERR_WORKSPACE, SA_ERR_ARGUMENT, SA_ERR_DEVICE = range(7)
+(SA_OK, SA_ERR_SHAPE, SA_ERR_NULL, SA_ERR_ALIGN, SA_ERR_WORKSPACE, SA_ERR_ARGUMENT, SA_ERR_DEVICE,
+ SA_ERR_UNSUPPORTED) = range(8)
 
 
 class SaShape(ctypes.Structure):
     """``sa_shape`` of include/sa.h."""
     _fields_ = [("batch", ctypes.c_int), ("T", ctypes.c_int), ("heads", ctypes.c_int),
                 ("kv_heads", ctypes.c_int), ("causal", ctypes.c_int), ("seqlens", ctypes.c_void_p),
-                ("block_order", ctypes.c_int)]
+                ("block_order", ctypes.c_int), ("v_rows", ctypes.c_int)]
 
 
 class SaError(RuntimeError):
@@ -85,9 +86,10 @@ def base2_scale(s: float) -> float:
     return float(np.float32(s / math.log(2.0)))
 
 
-def make_shape(batch, T, heads, kv_heads, causal=True, seqlens=None, block_order=0) -> SaShape:
-    """An sa_shape; `seqlens` is a device int32 tensor (kept alive by the shape) or None."""
-    sh = SaShape(batch, T, heads, kv_heads, int(bool(causal)), _ptr(seqlens), block_order)
+def make_shape(batch, T, heads, kv_heads, causal=True, seqlens=None, block_order=0, v_rows=0) -> SaShape:
+    """An sa_shape; `seqlens` is a device int32 tensor (kept alive by the shape) or None.
+    v_rows=1: the V operand is V [B][KV][T][64] (and dV comes back as [B][KV][T][64])."""
+    sh = SaShape(batch, T, heads, kv_heads, int(bool(causal)), _ptr(seqlens), block_order, v_rows)
     sh._keep = seqlens
     return sh
 
@@ -180,9 +182,11 @@ class Buffers:
     """Device tensors for one problem (torch allocations; the library allocates nothing).
 
     Inputs are copied from the float16 numpy arrays of ``workloads.make_inputs``;
-    outputs and the dS workspace are allocated empty."""
+    outputs and the dS workspace are allocated empty.  With ``v_rows`` the V
+    operand (attribute ``Vt``) holds V as rows [B][KV][T][64] and ``dVt``
+    receives dV in that layout."""
 
-    def __init__(self, inputs: dict, causal: bool, device="cuda", block_order=0):
+    def __init__(self, inputs: dict, causal: bool, device="cuda", block_order=0, v_rows=False):
         import torch
         Q = inputs["Q"]
         B, H, T, _ = Q.shape
@@ -191,17 +195,19 @@ class Buffers:
         dev = torch.device(device)
         def put(a):
             return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float16)).to(dev)
-        self.Q, self.K, self.Vt, self.dO = put(Q), put(inputs["K"]), put(inputs["Vt"]), put(inputs["dO"])
+        v = inputs["Vt"].transpose(0, 1, 3, 2) if v_rows else inputs["Vt"]
+        self.Q, self.K, self.Vt, self.dO = put(Q), put(inputs["K"]), put(v), put(inputs["dO"])
         sl = inputs.get("seqlens")
         self.seqlens = None if sl is None else torch.from_numpy(np.asarray(sl, dtype=np.int32)).to(dev)
-        self.shape = make_shape(B, T, H, KV, causal, self.seqlens, block_order)
+        self.v_rows = bool(v_rows)
+        self.shape = make_shape(B, T, H, KV, causal, self.seqlens, block_order, int(self.v_rows))
         f16, f32 = torch.float16, torch.float32
         self.O = torch.empty((B, T, H * 64), dtype=f16, device=dev)
         self.L = torch.empty((B, H, T), dtype=f32, device=dev)
         self.D = torch.empty((B, H, T), dtype=f32, device=dev)
         self.dQ = torch.empty((B, H, T, 64), dtype=f32, device=dev)
         self.dK = torch.empty((B, KV, T, 64), dtype=f32, device=dev)
-        self.dVt = torch.empty((B, KV, 64, T), dtype=f32, device=dev)
+        self.dVt = torch.empty((B, KV, T, 64) if v_rows else (B, KV, 64, T), dtype=f32, device=dev)
         self.ws_bytes = sa_backward_workspace_bytes(self.shape)
         self.dS = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
 

@@ -32,6 +32,7 @@ sa::Shape to_shape(const sa_shape* s) {
     r.causal = s->causal;
     r.seqlens = s->seqlens;
     r.block_order = s->block_order;
+    r.v_rows = s->v_rows;
     return r;
 }
 
@@ -46,6 +47,7 @@ sa_shape batch1_causal(int T, int heads, int kv_heads) {
     s.causal = 1;
     s.seqlens = nullptr;
     s.block_order = 0;
+    s.v_rows = 0;
     return s;
 }
 
@@ -59,7 +61,9 @@ sa_status sa_check_shape(const sa_shape* shape) {
     if (s.batch < 1 || s.T < 64 || s.T % 64 != 0 || s.T > (1 << 20)) return SA_ERR_SHAPE;
     if (s.heads < 1 || s.kv_heads < 1 || s.heads % s.kv_heads != 0 || s.heads > 65535) return SA_ERR_SHAPE;
     if ((long long)s.batch * s.heads > (1ll << 24)) return SA_ERR_SHAPE;
-    if ((s.causal != 0 && s.causal != 1) || (s.block_order != 0 && s.block_order != 1)) return SA_ERR_SHAPE;
+    if ((s.causal != 0 && s.causal != 1) || (s.block_order != 0 && s.block_order != 1) ||
+        (s.v_rows != 0 && s.v_rows != 1))
+        return SA_ERR_SHAPE;
     if (s.seqlens && ((uintptr_t)s.seqlens & 3u)) return SA_ERR_ALIGN;
     const sa::Shape sh = to_shape(shape);
     const size_t lim = (size_t)INT_MAX;
@@ -150,6 +154,7 @@ sa_status sa_query_pass(const sa_shape* shape, const void* dO, const void* O, co
     if (st != SA_OK) return st;
     if ((st = check_ptrs({dO, O, L, Q, K, Vt, D, dQ})) != SA_OK) return st;
     if (!scale_ok(c) || !scale_ok(s)) return SA_ERR_ARGUMENT;
+    if (shape->v_rows) return SA_ERR_UNSUPPORTED;
     return from_hip(sa::launch_query_pass(to_shape(shape), dO, O, L, Q, K, Vt, c, s, D, dQ, (hipStream_t)stream));
 }
 
@@ -160,6 +165,7 @@ sa_status sa_backward_two_pass(const sa_shape* shape, const void* dO, const void
     if (st != SA_OK) return st;
     if ((st = check_ptrs({dO, O, L, D, Q, K, Vt, dQ, dK, dVt})) != SA_OK) return st;
     if (!scale_ok(c) || !scale_ok(s)) return SA_ERR_ARGUMENT;
+    if (shape->v_rows) return SA_ERR_UNSUPPORTED;
     const sa::Shape sh = to_shape(shape);
     hipStream_t strm = (hipStream_t)stream;
     if ((st = from_hip(sa::launch_query_pass(sh, dO, O, L, Q, K, Vt, c, s, D, dQ, strm))) != SA_OK) return st;
@@ -175,6 +181,7 @@ const char* sa_status_string(int status) {
         case SA_ERR_WORKSPACE: return "dS workspace smaller than sa_backward_workspace_bytes";
         case SA_ERR_ARGUMENT: return "scale c or s is not finite and positive";
         case SA_ERR_DEVICE: return "a HIP kernel launch failed";
+        case SA_ERR_UNSUPPORTED: return "this entry point takes V^T only (shape v_rows must be 0)";
         default: return "unknown status";
     }
 }

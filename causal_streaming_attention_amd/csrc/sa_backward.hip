@@ -146,7 +146,7 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     const half_t* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ D,
     half_t* __restrict__ dS, float* __restrict__ dK, float* __restrict__ dVt,
     const int32_t* __restrict__ seqlens, float c, float s, int T, int H, int KV, int nkt, int BKV,
-    int block_order, long long tiles_per_head) {
+    int block_order, long long tiles_per_head, int v_rows) {
     constexpr int kThreads = 128 * GW;
     __shared__ __attribute__((aligned(16))) char smem[KeyLds<GW>::bytes];
 
@@ -186,9 +186,14 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
         for (int q4 = 0; q4 < 4; ++q4) kf[q4] = *(const half8*)(kp + 16 * q4);
     }
     // V^T as the B operand of dP = dO V^T: lane (key, hi) needs V^T[16 s + 8 hi + 0..7][key],
-    // a column of the V^T tile: stage the tile once and read it transposed.
+    // a row of V when V comes as rows, else a column of the V^T tile: stage
+    // that tile once and read it transposed.
     half8 vf[4];
-    {
+    if (v_rows) {
+        const half_t* vp = Vt + kv_off + (size_t)key * kHeadDim + 8 * hi;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) vf[q4] = *(const half8*)(vp + 16 * q4);
+    } else {
         half_t* vt_lds = (half_t*)smem;
         for (int chunk = tid; chunk < 512; chunk += kThreads) {
             int row = chunk >> 3, col = (chunk & 7) * 8;
@@ -428,6 +433,16 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     __syncthreads();
     to_lds(dvacc0, dvacc1);
     __syncthreads();
+    if (v_rows) {
+        for (int idx = tid; idx < 64 * 16; idx += kThreads) {  // dV[key][d]: 16 float4s per key
+            const int kk = idx >> 4, d4 = (idx & 15) * 4;
+            f32x4 v = *(const f32x4*)&red[kk * kRedRow + d4];
+#pragma unroll
+            for (int g = 1; g < GW; ++g) v += *(const f32x4*)&red[(g * 64 + kk) * kRedRow + d4];
+            *(f32x4*)(dVt + (key_row0 + kk) * kHeadDim + d4) = v;
+        }
+        return;
+    }
     for (int idx = tid; idx < 64 * 16; idx += kThreads) {  // dV^T[d][key]: 16 float4s per d row
         const int d = idx >> 4, k4 = (idx & 15) * 4;
         f32x4 v;
@@ -690,10 +705,10 @@ template <bool CAUSAL, bool VARLEN>
 void launch_key_gw(int GW, dim3 grid, hipStream_t stream, const half_t* Q, const half_t* K, const half_t* Vt,
                    const half_t* dO, const float* L, const float* D, half_t* dS, float* dK, float* dVt,
                    const int32_t* seqlens, float c, float s, int T, int H, int KV, int nkt, int BKV, int order,
-                   long long tph) {
+                   long long tph, int v_rows) {
 #define SA_KEY_LAUNCH(gw)                                                                                    \
     hipLaunchKernelGGL((sa_key_kernel<CAUSAL, VARLEN, gw>), grid, dim3(128 * gw), 0, stream, Q, K, Vt, dO, L, \
-                       D, dS, dK, dVt, seqlens, c, s, T, H, KV, nkt, BKV, order, tph)
+                       D, dS, dK, dVt, seqlens, c, s, T, H, KV, nkt, BKV, order, tph, v_rows)
     switch (GW) {
         case 4: SA_KEY_LAUNCH(4); break;
         case 3: SA_KEY_LAUNCH(3); break;
@@ -746,7 +761,7 @@ hipError_t launch_key_pass(const Shape& sh, const void* Q, const void* K, const 
         constexpr bool C = decltype(causal_tag)::value, V = decltype(varlen_tag)::value;
         launch_key_gw<C, V>(GW, grid, stream, (const half_t*)Q, (const half_t*)K, (const half_t*)Vt,
                             (const half_t*)dO, L, D, (half_t*)dS, dK, dVt, sh.seqlens, c, s, sh.T, sh.heads,
-                            sh.kv_heads, nkt, BKV, sh.block_order, tph);
+                            sh.kv_heads, nkt, BKV, sh.block_order, tph, sh.v_rows);
     };
     using T_ = std::true_type;
     using F_ = std::false_type;

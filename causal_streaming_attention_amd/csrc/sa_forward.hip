@@ -31,6 +31,8 @@
 // the query tiles (n - 1 - p, p) in pairs of equal causal length, with the
 // heads that share a kv head kept on one XCD (pair_schedule).
 #include "sa_device.h"
+#include <type_traits>
+
 #include "sa_internal.h"
 
 namespace sa {
@@ -73,16 +75,17 @@ __device__ __forceinline__ uint4 clear_tail(uint4 v, int keep) {
         SA_FWD_SLOT; SA_FWD_SLOT; SA_FWD_SLOT; SA_FWD_SLOT;       \
     } while (0)
 
-template <bool CAUSAL, bool VARLEN>
+template <bool CAUSAL, bool VARLEN, bool VROWS>
 __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
     const half_t* __restrict__ Q, const half_t* __restrict__ K, const half_t* __restrict__ Vt,
     half_t* __restrict__ O, float* __restrict__ L, const int32_t* __restrict__ seqlens, float c, int T,
     int H, int KV, int n_qtiles, int BH, int block_order) {
     // K tile j + 2 is staged while tile j + 1's scores are formed, and V^T
     // tile j + 1 while tile j - 1's products are summed: two K buffers and
-    // three V^T buffers (V^T tile j lives in buffer j % 3).
+    // three V^T buffers (V^T tile j lives in buffer j % 3).  VROWS: V comes
+    // as rows [T][64] like K and its tiles are staged like K's.
     __shared__ __attribute__((aligned(16))) half_t kls[2][kTileHalves];
-    __shared__ __attribute__((aligned(16))) half_t vls[3][kVTileHalves];
+    __shared__ __attribute__((aligned(16))) half_t vls[3][VROWS ? kTileHalves : kVTileHalves];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int l32 = lane & 31, hi = lane >> 5;
@@ -160,14 +163,29 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
         rb = *(const uint4*)(kt_ + row_b * kHeadDim);
     };
     auto load_v = [&](int j, uint4& ra, uint4& rb) {
-        ra = *(const uint4*)(Vp + (size_t)row_a * T + j * kTile + col8);
-        rb = *(const uint4*)(Vp + (size_t)row_b * T + j * kTile + col8);
+        if (VROWS) {
+            const half_t* vt_ = Vp + (size_t)(j * kTile) * kHeadDim + col8;
+            ra = *(const uint4*)(vt_ + row_a * kHeadDim);
+            rb = *(const uint4*)(vt_ + row_b * kHeadDim);
+        } else {
+            ra = *(const uint4*)(Vp + (size_t)row_a * T + j * kTile + col8);
+            rb = *(const uint4*)(Vp + (size_t)row_b * T + j * kTile + col8);
+        }
     };
     auto store_k = [&](int buf, const uint4& ra, const uint4& rb) {
         *(uint4*)&kls[buf][row_a * kLdsRow + col8] = ra;
         *(uint4*)&kls[buf][row_b * kLdsRow + col8] = rb;
     };
     auto store_v = [&](int j, int buf, uint4 ra, uint4 rb) {
+        if (VROWS) {
+            // rows are keys: keys at or past the length carry P = 0, so
+            // their V rows are cleared (the padding may hold anything)
+            if (VARLEN && j * kTile + row_a >= len) ra = make_uint4(0, 0, 0, 0);
+            if (VARLEN && j * kTile + row_b >= len) rb = make_uint4(0, 0, 0, 0);
+            *(uint4*)&vls[buf][row_a * kLdsRow + col8] = ra;
+            *(uint4*)&vls[buf][row_b * kLdsRow + col8] = rb;
+            return;
+        }
         if (VARLEN && j * kTile + col8 + 8 > len) {
             // keys at or past the length carry P = 0: clear their V entries
             ra = clear_tail(ra, len - (j * kTile + col8));
@@ -197,14 +215,23 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
     // four 16-key k-steps.  k-step s covers the tile's keys 16 s + 4 hi + 0..3
     // and 16 s + 8 + 4 hi + 0..3 (the score accumulator's order), and V^T's A
     // operand is read in that same order.
+    // VROWS: the same values come from the V row tile by transposed reads,
+    // lane (d, hi) getting keys 16 s + 4 hi + 0..3 (then + 8) of column d.
     auto pv = [&](const half_t* Vs, const uint32_t (&w)[16]) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const half8 pb = half8_from_words(w[4 * s], w[4 * s + 1], w[4 * s + 2], w[4 * s + 3]);
-            const half_t* v0 = Vs + l32 * kVRow + 16 * s + 4 * hi;
-            const half_t* v1 = v0 + 32 * kVRow;
-            oacc0 = mfma32(cat(*(const half4*)v0, *(const half4*)(v0 + 8)), pb, oacc0);
-            oacc1 = mfma32(cat(*(const half4*)v1, *(const half4*)(v1 + 8)), pb, oacc1);
+            if (VROWS) {
+                const half_t* r0 = Vs + tr_offset(lane, 16 * s, 16 * s + 4, 0);
+                const half_t* r1 = Vs + tr_offset(lane, 16 * s + 8, 16 * s + 12, 0);
+                oacc0 = mfma32(cat(lds_read_tr(r0), lds_read_tr(r1)), pb, oacc0);
+                oacc1 = mfma32(cat(lds_read_tr(r0 + 32), lds_read_tr(r1 + 32)), pb, oacc1);
+            } else {
+                const half_t* v0 = Vs + l32 * kVRow + 16 * s + 4 * hi;
+                const half_t* v1 = v0 + 32 * kVRow;
+                oacc0 = mfma32(cat(*(const half4*)v0, *(const half4*)(v0 + 8)), pb, oacc0);
+                oacc1 = mfma32(cat(*(const half4*)v1, *(const half4*)(v1 + 8)), pb, oacc1);
+            }
         }
     };
 
@@ -379,13 +406,18 @@ hipError_t launch_forward(const Shape& sh, const void* Q, const void* K, const v
                            sh.block_order);
     };
     const bool varlen = sh.seqlens != nullptr;
-    if (sh.causal) {
-        if (varlen) args(sa_forward_kernel<true, true>);
-        else args(sa_forward_kernel<true, false>);
-    } else {
-        if (varlen) args(sa_forward_kernel<false, true>);
-        else args(sa_forward_kernel<false, false>);
-    }
+    auto go = [&](auto rows_tag) {
+        constexpr bool R = decltype(rows_tag)::value;
+        if (sh.causal) {
+            if (varlen) args(sa_forward_kernel<true, true, R>);
+            else args(sa_forward_kernel<true, false, R>);
+        } else {
+            if (varlen) args(sa_forward_kernel<false, true, R>);
+            else args(sa_forward_kernel<false, false, R>);
+        }
+    };
+    if (sh.v_rows) go(std::true_type{});
+    else go(std::false_type{});
     return hipGetLastError();
 }
 

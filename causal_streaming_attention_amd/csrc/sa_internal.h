@@ -11,6 +11,7 @@ struct Shape {
     int batch, T, heads, kv_heads, causal;
     const int32_t* seqlens;  // device pointer or nullptr
     int block_order;
+    int v_rows;  // 1: V and dV as rows [T][64] (like K), 0: V^T and dV^T
 };
 
 // dS workspace geometry: one fp16 64x64 tile per (batch, query head, query

@@ -32,12 +32,14 @@
  *
  * Layouts (row-major, element offsets; B = batch, H = heads, KV = kv_heads):
  *   Q   fp16 [B][H][T][64]        K   fp16 [B][KV][T][64]
- *   Vt  fp16 [B][KV][64][T]       (V transposed, as the pages take it)
+ *   Vt  fp16 [B][KV][64][T]       (V transposed, as the pages take it;
+ *                                  with shape->v_rows = 1 it is V itself,
+ *                                  fp16 [B][KV][T][64], like K)
  *   O   fp16 [B][T][H*64]         (token-major, heads merged)
  *   L   fp32 [B][H][T]            (base-2 log-sum-exp; -inf on masked rows)
  *   dO  fp16 [B][H][T][64]        D   fp32 [B][H][T]
  *   dQ  fp32 [B][H][T][64]        dK  fp32 [B][KV][T][64]
- *   dVt fp32 [B][KV][64][T]
+ *   dVt fp32 [B][KV][64][T]       (shape->v_rows = 1: dV, fp32 [B][KV][T][64])
  *   dS  workspace, sa_backward_workspace_bytes() bytes, contents private.
  * Every pointer must be non-NULL and 16-byte aligned.
  *
@@ -66,7 +68,8 @@ typedef enum sa_status {
     SA_ERR_ALIGN = 3,      /* a pointer is not 16-byte aligned (seqlens: 4-byte) */
     SA_ERR_WORKSPACE = 4,  /* dS_bytes < sa_backward_workspace_bytes(shape) */
     SA_ERR_ARGUMENT = 5,   /* c or s not finite and positive */
-    SA_ERR_DEVICE = 6      /* a HIP launch failed (read, and so cleared, by hipGetLastError) */
+    SA_ERR_DEVICE = 6,     /* a HIP launch failed (read, and so cleared, by hipGetLastError) */
+    SA_ERR_UNSUPPORTED = 7 /* this entry point does not take the shape's v_rows = 1 */
 } sa_status;
 
 /*
@@ -75,7 +78,7 @@ typedef enum sa_status {
  * offset clause since every offset here is 64-bit):
  *   batch >= 1;  T >= 64 and T % 64 == 0;  heads >= 1;  kv_heads >= 1;
  *   heads % kv_heads == 0;  heads <= 65535;  batch * heads <= 2^24;
- *   T <= 2^20;  causal is 0 or 1;  block_order is 0 or 1.
+ *   T <= 2^20;  causal, block_order and v_rows are each 0 or 1.
  */
 typedef struct sa_shape {
     int batch;
@@ -89,6 +92,17 @@ typedef struct sa_shape {
     int block_order;          /* 0: heavy-first (longest causal blocks first,
                                  the pages' order 1); 1: natural order.  The
                                  results are bitwise identical either way. */
+    int v_rows;               /* 0: the V operand is V^T [B][KV][64][T] and
+                                 its gradient dV^T (the pages' layouts);
+                                 1: V [B][KV][T][64] and dV [B][KV][T][64],
+                                 rows like K (StreamingAttentionSM86 page,
+                                 the shared forward with V as rows: no
+                                 transposed copy of V, the staged V tile is
+                                 read transposed for P V).
+                                 The forward, the row terms, the key pass,
+                                 the dQ pass and sa_backward_ex take either;
+                                 the two-launch backward takes 0 only.
+                                 Results are bitwise identical either way. */
 } sa_shape;
 
 /* SA_OK if `shape` passes admission, else SA_ERR_SHAPE (SA_ERR_NULL if NULL).

@@ -23,12 +23,14 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_gpu(inputs, causal, block_order=0, backward=True, path="split"):
+def run_gpu(inputs, causal, block_order=0, backward=True, path="split", v_rows=False):
     """Forward (and backward) on cuda:0; returns the buffers object and numpy copies.
     path "split" is the three-launch backward through the dS workspace,
-    "two_pass" the two-launch backward that stores no dS."""
+    "two_pass" the two-launch backward that stores no dS.  v_rows: V goes in
+    as rows [B][KV][T][64]; dV comes back in that layout and is returned
+    transposed, as dVt, like the V^T path's."""
     import torch
-    buf = sa.Buffers(inputs, causal, block_order=block_order)
+    buf = sa.Buffers(inputs, causal, block_order=block_order, v_rows=v_rows)
     buf.forward(C)
     if backward and path == "split":
         buf.backward(C, SCALE)
@@ -43,6 +45,8 @@ def run_gpu(inputs, causal, block_order=0, backward=True, path="split"):
     }
     if backward:
         out.update({k: getattr(buf, k).cpu().numpy().astype(np.float64) for k in ("D", "dQ", "dK", "dVt")})
+        if v_rows:
+            out["dVt"] = np.ascontiguousarray(out["dVt"].transpose(0, 1, 3, 2))
     return buf, out
 
 

@@ -43,15 +43,15 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_header_compiles_as_plain_c(tmp_path):
     src = tmp_path / "use.c"
-    src.write_text('#include "sa.h"\nint main(void) { sa_shape s = {1, 64, 1, 1, 1, 0, 0};'
+    src.write_text('#include "sa.h"\nint main(void) { sa_shape s = {1, 64, 1, 1, 1, 0, 0, 0};'
                    ' return (int)sa_backward_workspace_bytes(&s) == 0; }\n')
     r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-c", str(src), "-I", os.path.join(ROOT, "include"),
                         "-o", str(tmp_path / "use.o")], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
 
 
-def shape(batch=1, T=128, heads=4, kv=2, causal=1, order=0, seqlens=None):
-    return sa.SaShape(batch, T, heads, kv, causal, seqlens, order)
+def shape(batch=1, T=128, heads=4, kv=2, causal=1, order=0, seqlens=None, v_rows=0):
+    return sa.SaShape(batch, T, heads, kv, causal, seqlens, order, v_rows)
 
 
 @pytest.mark.parametrize("kw,ok", [
@@ -68,6 +68,9 @@ def shape(batch=1, T=128, heads=4, kv=2, causal=1, order=0, seqlens=None):
     ({"heads": 65536, "kv": 1}, False),
     ({"heads": 32, "kv": 8}, True),
     ({"causal": 2}, False),
+    ({"v_rows": 1}, True),
+    ({"v_rows": 2}, False),
+    ({"v_rows": -1}, False),
     ({"order": 2}, False),
     ({"order": 1}, True),
     ({"batch": 1 << 20, "heads": 32, "kv": 8}, False),
@@ -162,6 +165,8 @@ def test_two_pass_entry_points_reject_bad_arguments(lib):
     assert query(q_ptrs, c=0.0) == sa.SA_ERR_ARGUMENT
     assert query(q_ptrs, sc=float("inf")) == sa.SA_ERR_ARGUMENT
     assert query(q_ptrs, sh=shape(T=100)) == sa.SA_ERR_SHAPE
+    # V as rows is taken by the three-launch path only; the check precedes any launch.
+    assert query(q_ptrs, sh=shape(v_rows=1)) == sa.SA_ERR_UNSUPPORTED
 
     b_ptrs = [FAKE] * 10  # dO O L D Q K Vt dQ dK dVt
 
@@ -176,12 +181,13 @@ def test_two_pass_entry_points_reject_bad_arguments(lib):
         assert two_pass(bad) == sa.SA_ERR_ALIGN
     assert two_pass(b_ptrs, sc=-1.0) == sa.SA_ERR_ARGUMENT
     assert two_pass(b_ptrs, sh=shape(heads=6, kv=4)) == sa.SA_ERR_SHAPE
+    assert two_pass(b_ptrs, sh=shape(v_rows=1)) == sa.SA_ERR_UNSUPPORTED
     assert lib.sa_backward_two_pass(None, *b_ptrs[:7], 0.18, 0.125, *b_ptrs[7:], None) == sa.SA_ERR_NULL
 
 
 def test_status_strings(lib):
-    for st in range(7):
-        assert sa.sa_status_string(st)
+    for st in range(8):
+        assert sa.sa_status_string(st) != "unknown status"
     assert sa.sa_status_string(99) == "unknown status"
 
 
