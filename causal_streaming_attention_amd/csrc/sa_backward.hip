@@ -354,8 +354,11 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
             dv[rg] = *(const f32x4*)(Ds + 8 * rg + 4 * hi);
         }
         // The previous item's products go into the matrix pipe behind these,
-        // one between every few of this item's vector instructions.
+        // one between every few of this item's vector instructions.  The
+        // wave runs that stretch at raised priority, so that of the two waves
+        // on a SIMD the one with matrix work in hand issues first.
         __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
         accumulate(t, wp, wd);
         float p[16], g[16];
 #pragma unroll
@@ -364,6 +367,7 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
             g[r] = p[r] * (pacc[r] - dv[r >> 2][r & 3]);
         }
         SA_KEY_INTERLEAVE();
+        __builtin_amdgcn_s_setprio(0);
         const bool need_mask = (CAUSAL && qb < kbase + 31) || (VARLEN && (qb + kSubRows > len || kbase + 32 > len));
         if (need_mask) {
 #pragma unroll

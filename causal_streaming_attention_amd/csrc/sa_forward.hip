@@ -268,6 +268,9 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
             // the other K buffer; after the wave's last tile they are formed
             // from whatever it holds and never used.  At j = 0 there is no
             // previous tile: pprev is zero and V^T tile 0 stands in.
+            // Raised wave priority over the interleaved stretch: of the two
+            // waves on a SIMD, the one with matrix work in hand issues first.
+            __builtin_amdgcn_s_setprio(1);
             scores(kls[(j + 1) & 1], nxt0, nxt1);
             pv(vls[j == 0 ? 0 : (j + 2) % 3], pprev);
 
@@ -303,6 +306,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
             lsum = __builtin_fmaf(lsum, alpha, psum);
             m = m_new;
             SA_FWD_INTERLEAVE();
+            __builtin_amdgcn_s_setprio(0);
         }
 
         // K_{j+2} replaces K_j (last read in the previous step) and V_{j+1}
