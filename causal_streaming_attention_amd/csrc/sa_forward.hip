@@ -47,6 +47,17 @@ constexpr int kTileHalves = kTile * kLdsRow; // one padded 64-row K tile in LDS
 // from sixteen consecutive rows then touch 32 distinct banks.
 constexpr int kVRow = 68;
 constexpr int kVTileHalves = kTile * kVRow;
+// A V row tile (V as rows [T][64]) is unpadded, 128-byte rows whose 16-byte
+// chunk c sits at chunk c ^ vr_key(r): the transposed reads of P V's operand
+// cover 4 rows x 2 chunks of an aligned group of 4 rows, and with bit 2 of
+// the key equal to bit 1 of the row the two rows of each parity (which share
+// banks, two 128-byte rows to the 256-byte bank row) land in different
+// 4-chunk halves.
+constexpr int kVRowsTileHalves = kTile * kHeadDim;
+__device__ __forceinline__ int vr_key(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int vr_off(int r, int col) {
+    return r * kHeadDim + (((col >> 3) ^ vr_key(r)) << 3) + (col & 7);
+}
 // The running maximum used for the exponents moves only when some row of the
 // wave sees a scaled score more than this far (base 2) above it, so P <= 2^8.
 constexpr float kMaxSlack = 8.0f;
@@ -85,7 +96,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
     // three V^T buffers (V^T tile j lives in buffer j % 3).  VROWS: V comes
     // as rows [T][64] like K and its tiles are staged like K's.
     __shared__ __attribute__((aligned(16))) half_t kls[2][kTileHalves];
-    __shared__ __attribute__((aligned(16))) half_t vls[3][VROWS ? kTileHalves : kVTileHalves];
+    __shared__ __attribute__((aligned(16))) half_t vls[3][VROWS ? kVRowsTileHalves : kVTileHalves];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int l32 = lane & 31, hi = lane >> 5;
@@ -182,8 +193,8 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
             // their V rows are cleared (the padding may hold anything)
             if (VARLEN && j * kTile + row_a >= len) ra = make_uint4(0, 0, 0, 0);
             if (VARLEN && j * kTile + row_b >= len) rb = make_uint4(0, 0, 0, 0);
-            *(uint4*)&vls[buf][row_a * kLdsRow + col8] = ra;
-            *(uint4*)&vls[buf][row_b * kLdsRow + col8] = rb;
+            *(uint4*)&vls[buf][vr_off(row_a, col8)] = ra;
+            *(uint4*)&vls[buf][vr_off(row_b, col8)] = rb;
             return;
         }
         if (VARLEN && j * kTile + col8 + 8 > len) {
@@ -215,6 +226,16 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
     // four 16-key k-steps.  k-step s covers the tile's keys 16 s + 4 hi + 0..3
     // and 16 s + 8 + 4 hi + 0..3 (the score accumulator's order), and V^T's A
     // operand is read in that same order.
+    // Lane offsets of the transposed V row reads at k-step 0: rows
+    // 4 hi + (lane % 16) / 4 and 8 more, columns d 0..31 then 32..63.
+    int vr_tr[4];
+    {
+        const int r = 4 * hi + ((lane & 15) >> 2), cl = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        vr_tr[0] = vr_off(r, cl);
+        vr_tr[1] = vr_off(r + 8, cl);
+        vr_tr[2] = vr_off(r, 32 + cl);
+        vr_tr[3] = vr_off(r + 8, 32 + cl);
+    }
     // VROWS: the same values come from the V row tile by transposed reads,
     // lane (d, hi) getting keys 16 s + 4 hi + 0..3 (then + 8) of column d.
     auto pv = [&](const half_t* Vs, const uint32_t (&w)[16]) {
@@ -222,10 +243,11 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
         for (int s = 0; s < 4; ++s) {
             const half8 pb = half8_from_words(w[4 * s], w[4 * s + 1], w[4 * s + 2], w[4 * s + 3]);
             if (VROWS) {
-                const half_t* r0 = Vs + tr_offset(lane, 16 * s, 16 * s + 4, 0);
-                const half_t* r1 = Vs + tr_offset(lane, 16 * s + 8, 16 * s + 12, 0);
-                oacc0 = mfma32(cat(lds_read_tr(r0), lds_read_tr(r1)), pb, oacc0);
-                oacc1 = mfma32(cat(lds_read_tr(r0 + 32), lds_read_tr(r1 + 32)), pb, oacc1);
+                // rows 16 s + 4 hi + (lane % 16) / 4 (+ 8): 16 rows on keeps
+                // the chunk key, so only the k-step moves the base
+                const half_t* vs = Vs + 16 * s * kHeadDim;
+                oacc0 = mfma32(cat(lds_read_tr(vs + vr_tr[0]), lds_read_tr(vs + vr_tr[1])), pb, oacc0);
+                oacc1 = mfma32(cat(lds_read_tr(vs + vr_tr[2]), lds_read_tr(vs + vr_tr[3])), pb, oacc1);
             } else {
                 const half_t* v0 = Vs + l32 * kVRow + 16 * s + 4 * hi;
                 const half_t* v1 = v0 + 32 * kVRow;
