@@ -80,6 +80,23 @@ def load_traffic(kernel: str, workload: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+def gpu_state():
+    """Shader/memory clocks and package power from rocm-smi (a child process), or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        d = json.loads(r.stdout)
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+    out = {}
+    for card, fields in d.items():
+        if isinstance(fields, dict):
+            out[card] = {k: v for k, v in fields.items()
+                         if any(t in k.lower() for t in ("sclk", "mclk", "power"))}
+    return out or None
+
+
 def cpu_baseline(w, x, budget_s: float = 10.0):
     """Time the binary64 oracle on the same inputs, one K/V head group (its G query
     heads of one sequence, the whole forward and backward) at a time, until about
@@ -106,7 +123,7 @@ def cpu_baseline(w, x, budget_s: float = 10.0):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": f"{what} of {w.name} (K/V head groups of {G} query heads, batch row by batch row): "
                       f"full forward and backward, {flops / 1e9:.2f} GFLOP in {dt:.1f} s",
-            "cpu": platform.processor() or _cpu_model()}
+            "cpu": _cpu_model() if _cpu_model() != "unknown" else platform.processor(), "nproc": os.cpu_count()}
 
 
 def _cpu_model():
@@ -250,6 +267,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    state_before = None if args.headline_only else gpu_state()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -265,6 +283,31 @@ def main():
     ms_per_step = max(step_ms, wall * 1e3 / args.steps)
     fl = kernel_flops(w, x["seqlens"])
     value = fl["total"] / (ms_per_step * 1e-3) / 1e12
+    state_after = None if args.headline_only else gpu_state()
+    bwd_ms = per["row_terms"] + per["key_pass"] + per["dq_pass"]
+    phases = {"forward_ms": round(per["forward"], 4), "backward_ms": round(bwd_ms, 4),
+              "forward_tflops": round(fl["forward"] / (per["forward"] * 1e-3) / 1e12, 1),
+              "backward_tflops": round((fl["key_pass"] + fl["dq_pass"]) / (bwd_ms * 1e-3) / 1e12, 1)}
+
+    # Cold steps: a 512 MiB scratch write between steps (outside the timed
+    # region) evicts the caches before each one.
+    cold = None
+    if not args.headline_only:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        cold_ms = []
+        for _ in range(min(args.steps, 5)):
+            scratch.fill_(1)
+            torch.cuda.synchronize()
+            ev[0].record(stream)
+            step()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            cold_ms.append(ev[0].elapsed_time(ev[1]))
+        del scratch
+        cms = float(np.median(cold_ms))
+        cold = {"ms_per_step": round(cms, 4), "tflops": round(fl["total"] / (cms * 1e-3) / 1e12, 2),
+                "steps": len(cold_ms), "note": "median; 512 MiB scratch write before each step, host-synchronised"}
 
     dominant = max(("forward", "key_pass", "dq_pass"), key=lambda n: per[n])
     achieved = fl[dominant] / (per[dominant] * 1e-3) / 1e12
@@ -365,8 +408,13 @@ def main():
         "pct_mfma_peak": round(100 * value / PEAK_TFLOPS, 2),
         "flops_per_step": fl["total"],
         "kernels": kernels,
+        "phases": phases,
         "roofline": roofline,
     }
+    if cold is not None:
+        out["cold"] = cold
+    if state_before is not None or state_after is not None:
+        out["gpu_state"] = {"before": state_before, "after": state_after}
     if two_pass is not None:
         out["two_pass_backward"] = two_pass
     if v_rows is not None:
