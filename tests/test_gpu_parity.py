@@ -44,6 +44,13 @@ SMALL = [
     ("varlen_full_b3_t256", 3, 256, 2, 2, False, [0, 1, 200]),
     ("varlen_causal_b4_t192", 4, 192, 4, 2, True, [65, 64, 130, 191]),
     ("varlen_gqa4_full_b2_t384", 2, 384, 4, 1, False, [383, 97]),
+    # edge cases: a single 64-key tile, lengths inside it and of zero, every
+    # sequence empty, and 16 query heads per K/V head (each wave slot walks
+    # four heads in turn)
+    ("single_tile_t64_causal", 2, 64, 2, 1, True, None),
+    ("single_tile_t64_varlen_full", 3, 64, 2, 2, False, [0, 17, 64]),
+    ("all_empty_varlen_causal", 2, 128, 2, 1, True, [0, 0]),
+    ("gqa16_t128_causal", 1, 128, 16, 1, True, None),
 ]
 
 
