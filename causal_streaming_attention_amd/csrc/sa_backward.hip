@@ -76,8 +76,11 @@ __global__ __launch_bounds__(kRowThreads) void sa_row_terms_kernel(const half_t*
 //   dS stored as fp16 (the words of dK's product) into its 64x64 tile
 //   dV^T += dO^T P, dK^T += Q^T dS (A = dO^T / Q^T by transposed LDS
 //   reads, in the permuted query order of P's / dS's accumulators).
-// The slots' dK and dV are then summed through LDS in slot order, dK scaled
-// by s, and stored with coalesced 16-byte writes.
+// The dV / dK products of a sub-tile are issued one sub-tile late, spread
+// through the next sub-tile's vector work at raised wave priority.  With V
+// as rows (v_rows), V's operand is loaded straight from its rows and dV is
+// written as rows.  The slots' dK and dV are then summed through LDS in slot
+// order, dK scaled by s, and stored with coalesced 16-byte writes.
 //
 // A staged 32 x 64 fp16 sub-tile has 128-byte rows whose 16-byte chunks are
 // permuted per row (swz below) so that its reads meet no bank conflict

@@ -10,8 +10,9 @@
 //
 // MI355X design (not the pages' SM86 one): a 256-thread workgroup (4 wave64s)
 // takes 128 queries of one query head; each wave owns 32 queries.  Each key
-// tile's K rows and V^T rows are staged once in LDS for all four waves with
-// coalesced 16-byte loads (K two tiles ahead, V^T one tile ahead).  A wave
+// tile's K rows and V^T rows (or V rows, when V comes as rows [T][64]: its
+// tile is then read transposed) are staged once in LDS for all four waves
+// with coalesced 16-byte loads (K two tiles ahead, V one tile ahead).  A wave
 // computes S^T = K Q^T with v_mfma_f32_32x32x16_f16 (A = K rows from LDS,
 // B = the wave's Q kept in registers), so every lane holds 32 scores of ONE
 // query: the row maximum is an in-lane max plus one v_permlane32_swap, the
@@ -24,7 +25,9 @@
 //
 // The loop is software-pipelined: while tile j's softmax runs on the vector
 // unit, the wave's matrix-core work is tile j + 1's scores and tile j - 1's
-// P V, issued between the softmax instructions.  The maximum used for the
+// P V, issued between the softmax instructions, at raised wave priority so
+// that of the two waves on a SIMD the one with matrix work issues first.  The
+// maximum used for the
 // exponents moves only when some row of the wave exceeds it by more than 8
 // (base 2), so P <= 2^8 and the O/l rescale is rare; O / l and L = m + log2 l
 // are the same quantities whichever maximum the exponents used.  Blocks take
