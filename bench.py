@@ -214,6 +214,42 @@ def summarize_profile(dirs, workload, command):
     print("\n".join(lines))
 
 
+SQ_COUNTERS = ["SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
+               "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"]
+
+
+def summarize_counters(d, workload, command):
+    """Write profiles/sq_counters_<workload>.txt from one rocprofv3 --pmc run of SQ_COUNTERS:
+    per-dispatch averages for each kernel, and the derived per-wave instruction mix and
+    the share of LDS-active cycles lost to bank conflicts."""
+    rows = _read_csv(_find(d, "counter_collection.csv"))
+    lines = [f"# rocprofv3 --pmc {' '.join(SQ_COUNTERS)} (per-dispatch averages), workload {workload}",
+             f"# command: {command}", ""]
+    for short, key in KERNEL_NAMES.items():
+        vals = {}
+        for r in rows:
+            if key in r["Kernel_Name"]:
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        if not vals:
+            continue
+        avg = {k: sum(v) / len(v) for k, v in vals.items()}
+        lines.append(f"{short}:")
+        for k in SQ_COUNTERS:
+            if k in avg:
+                lines.append(f"  {k:28s} {avg[k]:16.6g}")
+        waves = avg.get("SQ_WAVES", 0.0)
+        if waves > 0:
+            lines.append(f"  per wave: MFMA {avg.get('SQ_INSTS_MFMA', 0) / waves:.1f}, "
+                         f"VALU {avg.get('SQ_INSTS_VALU', 0) / waves:.1f}, LDS {avg.get('SQ_INSTS_LDS', 0) / waves:.1f}")
+        if avg.get("SQ_LDS_IDX_ACTIVE", 0) > 0:
+            lines.append(f"  LDS bank-conflict cycles / LDS-active cycles: "
+                         f"{avg.get('SQ_LDS_BANK_CONFLICT', 0) / avg['SQ_LDS_IDX_ACTIVE']:.3f}")
+        lines.append("")
+    with open(os.path.join(ROOT, "profiles", f"sq_counters_{workload}.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -231,10 +267,15 @@ def main():
     ap.add_argument("--summarize-profile", nargs="+", metavar="DIR",
                     help="summarize rocprofv3 output directories (kernel trace, then FETCH_SIZE and WRITE_SIZE "
                          "passes of a --calibrate-copy-mb run) into profiles/ and exit")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="summarize one rocprofv3 --pmc run of the SQ counters into profiles/ and exit")
     ap.add_argument("--profile-command", default="", help="command line recorded in the summaries")
     args = ap.parse_args()
     if args.summarize_profile:
         summarize_profile(args.summarize_profile, args.workload, args.profile_command)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.workload, args.profile_command)
         return
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
