@@ -22,8 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsa.so")
 _lib = None
 
-(SA_OK, SA_ERR_SHAPE, SA_ERR_NULL, SA_ERR_ALIGN, SA_ERR_WORKSPACE, SA_ERR_ARGUMENT, SA_ERR_DEVICE,
- SA_ERR_UNSUPPORTED) = range(8)
+SA_OK, SA_ERR_SHAPE, SA_ERR_NULL, SA_ERR_ALIGN, SA_ERR_WORKSPACE, SA_ERR_ARGUMENT, SA_ERR_DEVICE = range(7)
 
 
 class SaShape(ctypes.Structure):

@@ -154,7 +154,6 @@ sa_status sa_query_pass(const sa_shape* shape, const void* dO, const void* O, co
     if (st != SA_OK) return st;
     if ((st = check_ptrs({dO, O, L, Q, K, Vt, D, dQ})) != SA_OK) return st;
     if (!scale_ok(c) || !scale_ok(s)) return SA_ERR_ARGUMENT;
-    if (shape->v_rows) return SA_ERR_UNSUPPORTED;
     return from_hip(sa::launch_query_pass(to_shape(shape), dO, O, L, Q, K, Vt, c, s, D, dQ, (hipStream_t)stream));
 }
 
@@ -165,7 +164,6 @@ sa_status sa_backward_two_pass(const sa_shape* shape, const void* dO, const void
     if (st != SA_OK) return st;
     if ((st = check_ptrs({dO, O, L, D, Q, K, Vt, dQ, dK, dVt})) != SA_OK) return st;
     if (!scale_ok(c) || !scale_ok(s)) return SA_ERR_ARGUMENT;
-    if (shape->v_rows) return SA_ERR_UNSUPPORTED;
     const sa::Shape sh = to_shape(shape);
     hipStream_t strm = (hipStream_t)stream;
     if ((st = from_hip(sa::launch_query_pass(sh, dO, O, L, Q, K, Vt, c, s, D, dQ, strm))) != SA_OK) return st;
@@ -181,7 +179,6 @@ const char* sa_status_string(int status) {
         case SA_ERR_WORKSPACE: return "dS workspace smaller than sa_backward_workspace_bytes";
         case SA_ERR_ARGUMENT: return "scale c or s is not finite and positive";
         case SA_ERR_DEVICE: return "a HIP kernel launch failed";
-        case SA_ERR_UNSUPPORTED: return "this entry point takes V^T only (shape v_rows must be 0)";
         default: return "unknown status";
     }
 }

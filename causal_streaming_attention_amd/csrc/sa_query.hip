@@ -12,8 +12,9 @@
 //
 // MI355X design: a 256-thread workgroup (4 wave64s) takes 128 queries of one
 // query head, each wave 32 queries, and walks the key tiles with the K tile
-// and the V^T tile staged once in LDS for the four waves (16-byte loads one
-// tile ahead, double-buffered).  Per tile a wave runs 24 products on
+// and the V^T tile (or, with V as rows, the V row tile, staged and read like
+// K's) staged once in LDS for the four waves (16-byte loads one tile ahead,
+// double-buffered).  Per tile a wave runs 24 products on
 // v_mfma_f32_32x32x16_f16, all in the forward's orientation (lane = query):
 //   S^T  = K Q^T    (A = K rows, LDS; B = Q^T, registers)
 //   dP^T = V dO^T   (A = V rows, read transposed from the V^T tile; B = dO^T)
@@ -24,6 +25,8 @@
 // so P, dP and dS never leave registers.  Both tiles are stored unpadded
 // with the 16-byte chunks of each row permuted (swz), which keeps the row
 // reads and the transposed reads free of bank conflicts.
+#include <type_traits>
+
 #include "sa_device.h"
 #include "sa_internal.h"
 
@@ -64,14 +67,14 @@ __device__ __forceinline__ uint4 qp_clear_tail(uint4 v, int keep) {
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-template <bool CAUSAL, bool VARLEN>
+template <bool CAUSAL, bool VARLEN, bool VROWS>
 __global__ __launch_bounds__(kQpThreads, 2) void sa_query_kernel(
     const half_t* __restrict__ Q, const half_t* __restrict__ K, const half_t* __restrict__ Vt,
     const half_t* __restrict__ dO, const half_t* __restrict__ O, const float* __restrict__ L,
     float* __restrict__ D, float* __restrict__ dQ, const int32_t* __restrict__ seqlens, float c, float s,
     int T, int H, int KV, int n_qtiles, int BH, int block_order) {
     __shared__ __attribute__((aligned(16))) half_t kls[2][kQpTile];  // K tiles [key][d]
-    __shared__ __attribute__((aligned(16))) half_t vls[2][kQpTile];  // V^T tiles [d][key]
+    __shared__ __attribute__((aligned(16))) half_t vls[2][kQpTile];  // V^T tiles [d][key] (VROWS: V [key][d])
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int l32 = lane & 31, hi = lane >> 5;
@@ -104,8 +107,14 @@ __global__ __launch_bounds__(kQpThreads, 2) void sa_query_kernel(
         const half_t* kt_ = Kp + (size_t)(j * kTile) * kHeadDim + cc * 8;
         ka = *(const uint4*)(kt_ + row_a * kHeadDim);
         kb = *(const uint4*)(kt_ + row_b * kHeadDim);
-        va = *(const uint4*)(Vp + (size_t)row_a * T + j * kTile + cc * 8);
-        vb = *(const uint4*)(Vp + (size_t)row_b * T + j * kTile + cc * 8);
+        if (VROWS) {  // V as rows: its tile is staged exactly like K's
+            const half_t* vt_ = Vp + (size_t)(j * kTile) * kHeadDim + cc * 8;
+            va = *(const uint4*)(vt_ + row_a * kHeadDim);
+            vb = *(const uint4*)(vt_ + row_b * kHeadDim);
+        } else {
+            va = *(const uint4*)(Vp + (size_t)row_a * T + j * kTile + cc * 8);
+            vb = *(const uint4*)(Vp + (size_t)row_b * T + j * kTile + cc * 8);
+        }
     };
     auto store = [&](int j, int buf, uint4 ka, uint4 kb, uint4 va, uint4 vb) {
         if (VARLEN) {
@@ -114,7 +123,10 @@ __global__ __launch_bounds__(kQpThreads, 2) void sa_query_kernel(
             // value reaches a product
             if (j * kTile + row_a >= len) ka = make_uint4(0, 0, 0, 0);
             if (j * kTile + row_b >= len) kb = make_uint4(0, 0, 0, 0);
-            if (j * kTile + cc * 8 + 8 > len) {
+            if (VROWS) {
+                if (j * kTile + row_a >= len) va = make_uint4(0, 0, 0, 0);
+                if (j * kTile + row_b >= len) vb = make_uint4(0, 0, 0, 0);
+            } else if (j * kTile + cc * 8 + 8 > len) {
                 va = qp_clear_tail(va, len - (j * kTile + cc * 8));
                 vb = qp_clear_tail(vb, len - (j * kTile + cc * 8));
             }
@@ -198,11 +210,18 @@ __global__ __launch_bounds__(kQpThreads, 2) void sa_query_kernel(
                     const half8 a1 = *(const half8*)(Ks + qp_swz(32 + l32, 16 * t + 8 * hi));
                     s0 = mfma32(a0, qf[t], s0);
                     s1 = mfma32(a1, qf[t], s1);
-                    // A = V: lane (key, hi) holds V^T[16 t + 8 hi + 0..7][key].
-                    const half8 v0 = cat(lds_read_tr(Vs + qp_tr(lane, 16 * t, 16 * t + 8, 0)),
-                                         lds_read_tr(Vs + qp_tr(lane, 16 * t + 4, 16 * t + 12, 0)));
-                    const half8 v1 = cat(lds_read_tr(Vs + qp_tr(lane, 16 * t, 16 * t + 8, 32)),
-                                         lds_read_tr(Vs + qp_tr(lane, 16 * t + 4, 16 * t + 12, 32)));
+                    // A = V: lane (key, hi) holds V^T[16 t + 8 hi + 0..7][key],
+                    // a row read of a V row tile or a transposed read of V^T's.
+                    half8 v0, v1;
+                    if (VROWS) {
+                        v0 = *(const half8*)(Vs + qp_swz(l32, 16 * t + 8 * hi));
+                        v1 = *(const half8*)(Vs + qp_swz(32 + l32, 16 * t + 8 * hi));
+                    } else {
+                        v0 = cat(lds_read_tr(Vs + qp_tr(lane, 16 * t, 16 * t + 8, 0)),
+                                 lds_read_tr(Vs + qp_tr(lane, 16 * t + 4, 16 * t + 12, 0)));
+                        v1 = cat(lds_read_tr(Vs + qp_tr(lane, 16 * t, 16 * t + 8, 32)),
+                                 lds_read_tr(Vs + qp_tr(lane, 16 * t + 4, 16 * t + 12, 32)));
+                    }
                     p0 = mfma32(v0, of[t], p0);
                     p1 = mfma32(v1, of[t], p1);
                 }
@@ -294,13 +313,18 @@ hipError_t launch_query_pass(const Shape& sh, const void* dO, const void* O, con
                            sh.kv_heads, n_qtiles, BH, sh.block_order);
     };
     const bool varlen = sh.seqlens != nullptr;
-    if (sh.causal) {
-        if (varlen) go(sa_query_kernel<true, true>);
-        else go(sa_query_kernel<true, false>);
-    } else {
-        if (varlen) go(sa_query_kernel<false, true>);
-        else go(sa_query_kernel<false, false>);
-    }
+    auto pick = [&](auto rows_tag) {
+        constexpr bool R = decltype(rows_tag)::value;
+        if (sh.causal) {
+            if (varlen) go(sa_query_kernel<true, true, R>);
+            else go(sa_query_kernel<true, false, R>);
+        } else {
+            if (varlen) go(sa_query_kernel<false, true, R>);
+            else go(sa_query_kernel<false, false, R>);
+        }
+    };
+    if (sh.v_rows) pick(std::true_type{});
+    else pick(std::false_type{});
     return hipGetLastError();
 }
 

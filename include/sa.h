@@ -68,8 +68,7 @@ typedef enum sa_status {
     SA_ERR_ALIGN = 3,      /* a pointer is not 16-byte aligned (seqlens: 4-byte) */
     SA_ERR_WORKSPACE = 4,  /* dS_bytes < sa_backward_workspace_bytes(shape) */
     SA_ERR_ARGUMENT = 5,   /* c or s not finite and positive */
-    SA_ERR_DEVICE = 6,     /* a HIP launch failed (read, and so cleared, by hipGetLastError) */
-    SA_ERR_UNSUPPORTED = 7 /* this entry point does not take the shape's v_rows = 1 */
+    SA_ERR_DEVICE = 6      /* a HIP launch failed (read, and so cleared, by hipGetLastError) */
 } sa_status;
 
 /*
@@ -99,10 +98,8 @@ typedef struct sa_shape {
                                  the shared forward with V as rows: no
                                  transposed copy of V, the staged V tile is
                                  read transposed for P V).
-                                 The forward, the row terms, the key pass,
-                                 the dQ pass and sa_backward_ex take either;
-                                 the two-launch backward takes 0 only.
-                                 Results are bitwise identical either way. */
+                                 Every entry point takes either.  Results
+                                 are bitwise identical either way. */
 } sa_shape;
 
 /* SA_OK if `shape` passes admission, else SA_ERR_SHAPE (SA_ERR_NULL if NULL).

@@ -165,8 +165,6 @@ def test_two_pass_entry_points_reject_bad_arguments(lib):
     assert query(q_ptrs, c=0.0) == sa.SA_ERR_ARGUMENT
     assert query(q_ptrs, sc=float("inf")) == sa.SA_ERR_ARGUMENT
     assert query(q_ptrs, sh=shape(T=100)) == sa.SA_ERR_SHAPE
-    # V as rows is taken by the three-launch path only; the check precedes any launch.
-    assert query(q_ptrs, sh=shape(v_rows=1)) == sa.SA_ERR_UNSUPPORTED
 
     b_ptrs = [FAKE] * 10  # dO O L D Q K Vt dQ dK dVt
 
@@ -181,12 +179,11 @@ def test_two_pass_entry_points_reject_bad_arguments(lib):
         assert two_pass(bad) == sa.SA_ERR_ALIGN
     assert two_pass(b_ptrs, sc=-1.0) == sa.SA_ERR_ARGUMENT
     assert two_pass(b_ptrs, sh=shape(heads=6, kv=4)) == sa.SA_ERR_SHAPE
-    assert two_pass(b_ptrs, sh=shape(v_rows=1)) == sa.SA_ERR_UNSUPPORTED
     assert lib.sa_backward_two_pass(None, *b_ptrs[:7], 0.18, 0.125, *b_ptrs[7:], None) == sa.SA_ERR_NULL
 
 
 def test_status_strings(lib):
-    for st in range(8):
+    for st in range(7):
         assert sa.sa_status_string(st) != "unknown status"
     assert sa.sa_status_string(99) == "unknown status"
 

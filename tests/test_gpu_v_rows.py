@@ -72,3 +72,16 @@ def test_v_rows_padding_garbage_does_not_leak():
         _, got = run_gpu(dirty, causal, v_rows=True)
         for k in clean:
             assert np.array_equal(clean[k], got[k]), (causal, k)
+
+
+@pytest.mark.parametrize("name,B,T,H,KV,causal,seqlens", CASES, ids=[c[0] for c in CASES])
+def test_v_rows_two_pass_backward(name, B, T, H, KV, causal, seqlens):
+    """The two-launch backward (query pass + key pass without dS) with V as rows."""
+    say(f"case v_rows two-pass {name}")
+    x = make_inputs(B, T, H, KV, seed=400 + T + H, seqlens=seqlens)
+    _, rows = run_gpu(x, causal, path="two_pass", v_rows=True)
+    _, cols = run_gpu(x, causal, path="two_pass")
+    _same(rows, cols, name)
+    ref = full_reference(x, causal)
+    for k in ("dQ", "dK", "dVt"):
+        check_grad(k, rows[k], ref[k], name)
