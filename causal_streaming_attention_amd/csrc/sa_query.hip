@@ -22,7 +22,9 @@
 //                     key order of the score accumulator; B = dS^T packed to
 //                     binary16 straight from the accumulator, as the forward
 //                     feeds P to P V)
-// so P, dP and dS never leave registers.  Both tiles are stored unpadded
+// so P, dP and dS never leave registers.  A tile's dQ products are issued
+// one tile late, spread through the next tile's vector work at raised wave
+// priority (K tiles in a three-slot ring so the late reads stay valid).  Both tiles are stored unpadded
 // with the 16-byte chunks of each row permuted (swz), which keeps the row
 // reads and the transposed reads free of bank conflicts.
 #include <type_traits>
@@ -67,13 +69,25 @@ __device__ __forceinline__ uint4 qp_clear_tail(uint4 v, int keep) {
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Issue-order hint for one tile: the previous tile's 8 dQ products spread
+// through this tile's exponentials and dS arithmetic.
+#define SA_QP_SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+#define SA_QP_SLOT SA_QP_SGB(0x008, 1); SA_QP_SGB(0x002, 12)
+#define SA_QP_INTERLEAVE()                                    \
+    do {                                                      \
+        SA_QP_SLOT; SA_QP_SLOT; SA_QP_SLOT; SA_QP_SLOT;       \
+        SA_QP_SLOT; SA_QP_SLOT; SA_QP_SLOT; SA_QP_SLOT;       \
+    } while (0)
+
 template <bool CAUSAL, bool VARLEN, bool VROWS>
 __global__ __launch_bounds__(kQpThreads, 2) void sa_query_kernel(
     const half_t* __restrict__ Q, const half_t* __restrict__ K, const half_t* __restrict__ Vt,
     const half_t* __restrict__ dO, const half_t* __restrict__ O, const float* __restrict__ L,
     float* __restrict__ D, float* __restrict__ dQ, const int32_t* __restrict__ seqlens, float c, float s,
     int T, int H, int KV, int n_qtiles, int BH, int block_order) {
-    __shared__ __attribute__((aligned(16))) half_t kls[2][kQpTile];  // K tiles [key][d]
+    // K tile j lives in buffer j % 3: its dQ products are issued one tile late,
+    // beside the next tile's vector work, while tile j + 1 is staged.
+    __shared__ __attribute__((aligned(16))) half_t kls[3][kQpTile];  // K tiles [key][d]
     __shared__ __attribute__((aligned(16))) half_t vls[2][kQpTile];  // V^T tiles [d][key] (VROWS: V [key][d])
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -116,7 +130,7 @@ __global__ __launch_bounds__(kQpThreads, 2) void sa_query_kernel(
             vb = *(const uint4*)(Vp + (size_t)row_b * T + j * kTile + cc * 8);
         }
     };
-    auto store = [&](int j, int buf, uint4 ka, uint4 kb, uint4 va, uint4 vb) {
+    auto store = [&](int j, int kbuf, int buf, uint4 ka, uint4 kb, uint4 va, uint4 vb) {
         if (VARLEN) {
             // keys at or past the length: P and dS are masked to zero, and
             // their K rows and V^T columns are cleared so that no padding
@@ -131,8 +145,8 @@ __global__ __launch_bounds__(kQpThreads, 2) void sa_query_kernel(
                 vb = qp_clear_tail(vb, len - (j * kTile + cc * 8));
             }
         }
-        *(uint4*)&kls[buf][qp_swz(row_a, cc * 8)] = ka;
-        *(uint4*)&kls[buf][qp_swz(row_b, cc * 8)] = kb;
+        *(uint4*)&kls[kbuf][qp_swz(row_a, cc * 8)] = ka;
+        *(uint4*)&kls[kbuf][qp_swz(row_b, cc * 8)] = kb;
         *(uint4*)&vls[buf][qp_swz(row_a, cc * 8)] = va;
         *(uint4*)&vls[buf][qp_swz(row_b, cc * 8)] = vb;
     };
@@ -189,18 +203,43 @@ __global__ __launch_bounds__(kQpThreads, 2) void sa_query_kernel(
         if (n_kt > 0) {
             uint4 ka, kb, va, vb;
             load(0, ka, kb, va, vb);
-            store(0, 0, ka, kb, va, vb);
+            store(0, 0, 0, ka, kb, va, vb);
         }
         __syncthreads();
         vm_wait_all();  // the staged tile and Q, dO have landed (see the forward)
 
+        // dQ^T += K^T dS^T for one tile.  k-step t covers the tile's keys
+        // 16 t + 4 hi + 0..3 and 16 t + 8 + 4 hi + 0..3 (the accumulator's
+        // order); K^T's A operand is read transposed in that same order.
+        auto dq_products = [&](const half_t* Ks, const uint32_t (&w)[16]) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const half8 pb = half8_from_words(w[4 * t], w[4 * t + 1], w[4 * t + 2], w[4 * t + 3]);
+                const half8 k0 = cat(lds_read_tr(Ks + qp_tr(lane, 16 * t, 16 * t + 4, 0)),
+                                     lds_read_tr(Ks + qp_tr(lane, 16 * t + 8, 16 * t + 12, 0)));
+                const half8 k1 = cat(lds_read_tr(Ks + qp_tr(lane, 16 * t, 16 * t + 4, 32)),
+                                     lds_read_tr(Ks + qp_tr(lane, 16 * t + 8, 16 * t + 12, 32)));
+                dq0 = mfma32(k0, pb, dq0);
+                dq1 = mfma32(k1, pb, dq1);
+            }
+        };
+
+        // dS of the previous tile, packed (the B operand of its dQ products).
+        // Before the first tile it is zero and tile 0's K (finite) stands in,
+        // so those products add exact zeros.
+        uint32_t wprev[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) wprev[i] = 0u;
+        int kcur = 0, kprev = 0;  // ring positions of K tiles j and j - 1
         for (int j = 0; j < n_kt; ++j) {
             const int buf = j & 1;
             const bool more = j + 1 < n_kt;
+            const int knext = kcur == 2 ? 0 : kcur + 1;
             uint4 ka, kb, va, vb;
             if (more) load(j + 1, ka, kb, va, vb);
             if (j < n_kt_w) {
-                const half_t* Ks = kls[buf];
+                __builtin_amdgcn_s_setprio(1);
+                const half_t* Ks = kls[kcur];
                 const half_t* Vs = vls[buf];
                 // S^T = K Q^T and dP^T = V dO^T for the tile's two 32-key blocks.
                 f32x16 s0 = zero16(), s1 = zero16(), p0 = zero16(), p1 = zero16();
@@ -225,55 +264,55 @@ __global__ __launch_bounds__(kQpThreads, 2) void sa_query_kernel(
                     p0 = mfma32(v0, of[t], p0);
                     p1 = mfma32(v1, of[t], p1);
                 }
+                // The previous tile's dQ products go into the matrix pipe
+                // behind these, spread through this tile's vector work.
+                __builtin_amdgcn_sched_barrier(0);
+                dq_products(kls[j == 0 ? kcur : kprev], wprev);
                 // P = 2^(S c - L), dS = P (dP - D); masked elements are
                 // selected to exact zeros (never multiplied: padding may hold
                 // anything).  Lane holds key 8 (r / 4) + 4 hi + r % 4 (+ 32 for
                 // the second block) of query q.
+                float g0[16], g1[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    g0[r] = exp2_fast(__builtin_fmaf(s0[r], c, negL)) * (p0[r] - Dq);
+                    g1[r] = exp2_fast(__builtin_fmaf(s1[r], c, negL)) * (p1[r] - Dq);
+                }
+                SA_QP_INTERLEAVE();
+                __builtin_amdgcn_s_setprio(0);
                 const int key0 = j * kTile;
                 const bool need_mask = (CAUSAL && key0 + kTile - 1 > qw) ||
                                        (VARLEN && (key0 + kTile > len || qw + 32 > len));
-                uint32_t w[16];
+                if (need_mask) {
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    float g[4];
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const float pa = exp2_fast(__builtin_fmaf(s0[r + e], c, negL));
-                        const float pb = exp2_fast(__builtin_fmaf(s1[r + e], c, negL));
-                        g[e] = pa * (p0[r + e] - Dq);
-                        g[2 + e] = pb * (p1[r + e] - Dq);
+                    for (int r = 0; r < 16; ++r) {
+                        const int k0 = key0 + 8 * (r >> 2) + 4 * hi + (r & 3), k1 = k0 + 32;
+                        const bool m0 = (CAUSAL && k0 > q) || (VARLEN && (k0 >= len || q >= len));
+                        const bool m1 = (CAUSAL && k1 > q) || (VARLEN && (k1 >= len || q >= len));
+                        g0[r] = m0 ? 0.0f : g0[r];
+                        g1[r] = m1 ? 0.0f : g1[r];
                     }
-                    if (need_mask) {
-#pragma unroll
-                        for (int e = 0; e < 2; ++e) {
-                            const int k0 = key0 + 8 * ((r + e) >> 2) + 4 * hi + ((r + e) & 3), k1 = k0 + 32;
-                            const bool m0 = (CAUSAL && k0 > q) || (VARLEN && (k0 >= len || q >= len));
-                            const bool m1 = (CAUSAL && k1 > q) || (VARLEN && (k1 >= len || q >= len));
-                            g[e] = m0 ? 0.0f : g[e];
-                            g[2 + e] = m1 ? 0.0f : g[2 + e];
-                        }
-                    }
-                    w[r >> 1] = pack_half2(g[0], g[1]);
-                    w[8 + (r >> 1)] = pack_half2(g[2], g[3]);
                 }
-                // dQ^T += K^T dS^T.  k-step t covers the tile's keys 16 t + 4 hi
-                // + 0..3 and 16 t + 8 + 4 hi + 0..3 (the accumulator's order);
-                // K^T's A operand is read transposed in that same order.
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const half8 pb = half8_from_words(w[4 * t], w[4 * t + 1], w[4 * t + 2], w[4 * t + 3]);
-                    const half8 k0 = cat(lds_read_tr(Ks + qp_tr(lane, 16 * t, 16 * t + 4, 0)),
-                                         lds_read_tr(Ks + qp_tr(lane, 16 * t + 8, 16 * t + 12, 0)));
-                    const half8 k1 = cat(lds_read_tr(Ks + qp_tr(lane, 16 * t, 16 * t + 4, 32)),
-                                         lds_read_tr(Ks + qp_tr(lane, 16 * t + 8, 16 * t + 12, 32)));
-                    dq0 = mfma32(k0, pb, dq0);
-                    dq1 = mfma32(k1, pb, dq1);
+                for (int i = 0; i < 8; ++i) {
+                    wprev[i] = pack_half2(g0[2 * i], g0[2 * i + 1]);
+                    wprev[8 + i] = pack_half2(g1[2 * i], g1[2 * i + 1]);
                 }
+            } else if (j == n_kt_w && j > 0) {
+                // The wave's last tile's products (its K tile is not restaged
+                // before the next step ends).
+                dq_products(kls[kprev], wprev);
             }
-            if (more) store(j + 1, buf ^ 1, ka, kb, va, vb);
+            // Tile j + 1 goes to K ring slot j + 1 (which held tile j - 2,
+            // last read in the previous step) and V buffer buf ^ 1.
+            if (more) store(j + 1, knext, buf ^ 1, ka, kb, va, vb);
             vm_wait_all();  // nothing is outstanding here; keeps the compiler's count exact
             __syncthreads();
+            kprev = kcur;
+            kcur = knext;
         }
+        // A wave that formed the last tile adds its products here.
+        if (n_kt_w == n_kt && n_kt > 0) dq_products(kls[kprev], wprev);
 
         if (!wave_rows) return;
         // dQ = s dQ^T: lane holds d = 8 (r / 4) + 4 hi + r % 4 of query q.
