@@ -254,7 +254,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=150,
+                    help="untimed steps first; the shader clock ramps up over the first ~60 steps (~30 ms)")
     ap.add_argument("--workload", default="causal_gqa_t4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--block-order", type=int, default=0)
@@ -305,28 +306,45 @@ def main():
         sa.sa_dq_pass(sh, buf.K, buf.dS, buf.ws_bytes, SCALE, buf.dQ, stream)
         if ev: ev[4].record(stream)
 
+    def timed(step_fn, n_kernels):
+        """K steps between one pair of events (the step time: max of the events' and the host's clock), then
+        K more steps with an event between launches for the per-kernel averages.  Events between the
+        launches cost the step about 10 us, so the step time is taken without them."""
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        a.record(stream)
+        for _ in range(args.steps):
+            step_fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        step_ms = max(a.elapsed_time(b) / args.steps, wall_ms)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_kernels + 1)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for k in range(args.steps):
+            step_fn(evs[k])
+        torch.cuda.synchronize()
+        per_k = [float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
+                 for i in range(n_kernels)]
+        with_events = float(np.mean([evs[k][0].elapsed_time(evs[k][n_kernels]) for k in range(args.steps)]))
+        return step_ms, per_k, with_events
+
+    # The clock snapshot (a child process, during which the GPU idles and its clock drops) is taken before
+    # the warm-up, so that the timed steps follow the warm-up directly.
+    state_before = None if args.headline_only else gpu_state()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    state_before = None if args.headline_only else gpu_state()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(events[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
     names = ["forward", "row_terms", "key_pass", "dq_pass"]
-    per = {n: float(np.mean([events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps)]))
-           for i, n in enumerate(names)}
-    step_ms = float(np.mean([events[k][0].elapsed_time(events[k][4]) for k in range(args.steps)]))
-    ms_per_step = max(step_ms, wall * 1e3 / args.steps)
+    ms_per_step, per_list, step_with_events = timed(step, len(names))
+    per = dict(zip(names, per_list))
     fl = kernel_flops(w, x["seqlens"])
     value = fl["total"] / (ms_per_step * 1e-3) / 1e12
     state_after = None if args.headline_only else gpu_state()
     bwd_ms = per["row_terms"] + per["key_pass"] + per["dq_pass"]
-    phases = {"forward_ms": round(per["forward"], 4), "backward_ms": round(bwd_ms, 4),
+    phases = {"step_ms_with_kernel_events": round(step_with_events, 4),
+              "forward_ms": round(per["forward"], 4), "backward_ms": round(bwd_ms, 4),
               "forward_tflops": round(fl["forward"] / (per["forward"] * 1e-3) / 1e12, 1),
               "backward_tflops": round((fl["key_pass"] + fl["dq_pass"]) / (bwd_ms * 1e-3) / 1e12, 1)}
 
@@ -385,15 +403,9 @@ def main():
     if not args.headline_only:
         for _ in range(args.warmup):
             step2()
-        events2 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        for k in range(args.steps):
-            step2(events2[k])
-        torch.cuda.synchronize()
         names2 = ["forward", "query_pass", "key_pass_no_ds"]
-        per2 = {n: float(np.mean([events2[k][i].elapsed_time(events2[k][i + 1]) for k in range(args.steps)]))
-                for i, n in enumerate(names2)}
-        step2_ms = float(np.mean([events2[k][0].elapsed_time(events2[k][3]) for k in range(args.steps)]))
+        step2_ms, per2_list, _ = timed(step2, len(names2))
+        per2 = dict(zip(names2, per2_list))
         two_pass = {"ms_per_step": round(step2_ms, 4),
                     "tflops": round(fl["total"] / (step2_ms * 1e-3) / 1e12, 2),
                     "kernels_ms": {n: round(per2[n], 4) for n in names2},
@@ -418,14 +430,8 @@ def main():
 
         for _ in range(args.warmup):
             step3()
-        events3 = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        for k in range(args.steps):
-            step3(events3[k])
-        torch.cuda.synchronize()
-        per3 = {n: float(np.mean([events3[k][i].elapsed_time(events3[k][i + 1]) for k in range(args.steps)]))
-                for i, n in enumerate(names)}
-        step3_ms = float(np.mean([events3[k][0].elapsed_time(events3[k][4]) for k in range(args.steps)]))
+        step3_ms, per3_list, _ = timed(step3, len(names))
+        per3 = dict(zip(names, per3_list))
         v_rows = {"ms_per_step": round(step3_ms, 4),
                   "tflops": round(fl["total"] / (step3_ms * 1e-3) / 1e12, 2),
                   "kernels_ms": {n: round(per3[n], 4) for n in names},
