@@ -85,6 +85,11 @@ __device__ __forceinline__ void pair_schedule(int block, int n_groups, int group
     }
 }
 
+// Word 3 of a raw buffer resource on gfx950 (32-bit data format, no swizzle,
+// no index stride): loads address base + voffset + soffset, bounded by the
+// record count in bytes.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
 // Round to nearest even binary16.
 __device__ __forceinline__ half_t to_half(float x) { return (half_t)x; }
 

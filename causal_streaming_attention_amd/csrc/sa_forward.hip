@@ -170,21 +170,27 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
 
     // Staging: 512 16-byte chunks per 64x64 tile; thread tid moves chunks
     // (row_a, col8) and (row_a + 32, col8) of a K tile and of a V^T tile.
+    // They are buffer loads over the (batch, kv head) slice: the thread's
+    // part of each address is a fixed register offset and the tile's part a
+    // scalar one, so the loop spends no vector instructions on addresses.
     const int row_a = tid >> 3, row_b = row_a + 32, col8 = (tid & 7) * 8;
+    const int slice_bytes = T * kHeadDim * 2;
+    const __amdgpu_buffer_rsrc_t k_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)Kp, (short)0, slice_bytes, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t v_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)Vp, (short)0, slice_bytes, kBufferRsrcWord3);
+    const int k_off_a = (row_a * kHeadDim + col8) * 2, k_off_b = (row_b * kHeadDim + col8) * 2;
+    const int v_off_a = VROWS ? k_off_a : (row_a * T + col8) * 2;
+    const int v_off_b = VROWS ? k_off_b : (row_b * T + col8) * 2;
     auto load_k = [&](int j, uint4& ra, uint4& rb) {
-        const half_t* kt_ = Kp + (size_t)(j * kTile) * kHeadDim + col8;
-        ra = *(const uint4*)(kt_ + row_a * kHeadDim);
-        rb = *(const uint4*)(kt_ + row_b * kHeadDim);
+        const int tile = j * kTile * kHeadDim * 2;
+        ra = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, k_off_a, tile, 0));
+        rb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, k_off_b, tile, 0));
     };
     auto load_v = [&](int j, uint4& ra, uint4& rb) {
-        if (VROWS) {
-            const half_t* vt_ = Vp + (size_t)(j * kTile) * kHeadDim + col8;
-            ra = *(const uint4*)(vt_ + row_a * kHeadDim);
-            rb = *(const uint4*)(vt_ + row_b * kHeadDim);
-        } else {
-            ra = *(const uint4*)(Vp + (size_t)row_a * T + j * kTile + col8);
-            rb = *(const uint4*)(Vp + (size_t)row_b * T + j * kTile + col8);
-        }
+        const int tile = VROWS ? j * kTile * kHeadDim * 2 : j * kTile * 2;
+        ra = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(v_rsrc, v_off_a, tile, 0));
+        rb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(v_rsrc, v_off_b, tile, 0));
     };
     auto store_k = [&](int buf, const uint4& ra, const uint4& rb) {
         *(uint4*)&kls[buf][row_a * kLdsRow + col8] = ra;
