@@ -132,12 +132,12 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void dma16(const void* g, char* lds_wave_base) {
     __builtin_amdgcn_global_load_lds(g, (lds_void*)((__attribute__((address_space(3))) char*)lds_wave_base), 16, 0, 0);
 }
-// 16-byte direct load at g + OFF into LDS at lds_wave_base + OFF + 16 lane:
-// the offset field moves both addresses.
+// 16-byte buffer load at voffset + OFF within the resource into LDS at
+// lds_wave_base + OFF + 16 lane (the offset field moves both addresses).
 template <int OFF>
-__device__ __forceinline__ void dma16_at(const void* g, char* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)((__attribute__((address_space(3))) char*)lds_wave_base), 16, OFF,
-                                     0);
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voffset, char* lds_wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)((__attribute__((address_space(3))) char*)lds_wave_base),
+                                             16, voffset, 0, OFF, 0);
 }
 __device__ __forceinline__ void dma4(const void* g, char* lds_wave_base) {
     __builtin_amdgcn_global_load_lds(g, (lds_void*)((__attribute__((address_space(3))) char*)lds_wave_base), 4, 0, 0);
@@ -224,19 +224,24 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     // differ by 2 KB in memory and in LDS: the instruction's offset field.
     const uint32_t dma_off0 = (uint32_t)(dma_row * kHeadDim + ((lane & 7) ^ swz_key(dma_row)) * 8) * 2u;
     const uint32_t dma_off1 = (uint32_t)(dma_row * kHeadDim + ((lane & 7) ^ swz_key(dma_row + 8)) * 8) * 2u;
+    // The item's Q and dO rows as buffer resources built on the scalar unit:
+    // their loads take the fixed per-lane offsets, so no vector instruction
+    // forms their addresses.
     auto issue_item = [&](int head, int sub, int buf) {
         const size_t rowbase = ((size_t)b * H + head) * T + (size_t)sub * kSubRows;
-        const char* qrows = (const char*)(Q + rowbase * kHeadDim);
-        const char* orows = (const char*)(dO + rowbase * kHeadDim);
+        const __amdgpu_buffer_rsrc_t qr =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(Q + rowbase * kHeadDim), (short)0, kSubBytes, kBufferRsrcWord3);
+        const __amdgpu_buffer_rsrc_t orr =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(dO + rowbase * kHeadDim), (short)0, kSubBytes, kBufferRsrcWord3);
         char* base = wstage + buf * kItemBytes;
-        dma16_at<0>(qrows + dma_off0, base);
-        dma16_at<1024>(qrows + dma_off1, base);
-        dma16_at<2048>(qrows + dma_off0, base);
-        dma16_at<3072>(qrows + dma_off1, base);
-        dma16_at<0>(orows + dma_off0, base + kSubBytes);
-        dma16_at<1024>(orows + dma_off1, base + kSubBytes);
-        dma16_at<2048>(orows + dma_off0, base + kSubBytes);
-        dma16_at<3072>(orows + dma_off1, base + kSubBytes);
+        dma16_buf<0>(qr, dma_off0, base);
+        dma16_buf<1024>(qr, dma_off1, base);
+        dma16_buf<2048>(qr, dma_off0, base);
+        dma16_buf<3072>(qr, dma_off1, base);
+        dma16_buf<0>(orr, dma_off0, base + kSubBytes);
+        dma16_buf<1024>(orr, dma_off1, base + kSubBytes);
+        dma16_buf<2048>(orr, dma_off0, base + kSubBytes);
+        dma16_buf<3072>(orr, dma_off1, base + kSubBytes);
         const float* src = (lane < 32) ? (L + rowbase + lane) : (D + rowbase + (lane - 32));
         dma4(src, base + 2 * kSubBytes);
     };
