@@ -115,20 +115,25 @@ __global__ __launch_bounds__(kQpThreads, 2) void sa_query_kernel(
     const half_t* Vp = Vt + kv_off;
 
     // Staging: thread tid moves 16-byte chunks (row_a, cc) and (row_a + 32, cc)
-    // of a K tile (rows = keys) and of a V^T tile (rows = d, columns = keys).
+    // of a K tile (rows = keys) and of a V^T tile (rows = d, columns = keys),
+    // or of a V row tile, staged exactly like K's.  Buffer loads over the
+    // (batch, kv head) slice: a fixed per-lane register offset and a scalar
+    // tile offset, so the loop forms no addresses on the vector unit.
     const int row_a = tid >> 3, row_b = row_a + 32, cc = tid & 7;
+    const int slice_bytes = T * kHeadDim * 2;
+    const __amdgpu_buffer_rsrc_t k_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)Kp, (short)0, slice_bytes, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t v_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)Vp, (short)0, slice_bytes, kBufferRsrcWord3);
+    const int k_off_a = (row_a * kHeadDim + cc * 8) * 2, k_off_b = (row_b * kHeadDim + cc * 8) * 2;
+    const int v_off_a = VROWS ? k_off_a : (row_a * T + cc * 8) * 2;
+    const int v_off_b = VROWS ? k_off_b : (row_b * T + cc * 8) * 2;
     auto load = [&](int j, uint4& ka, uint4& kb, uint4& va, uint4& vb) {
-        const half_t* kt_ = Kp + (size_t)(j * kTile) * kHeadDim + cc * 8;
-        ka = *(const uint4*)(kt_ + row_a * kHeadDim);
-        kb = *(const uint4*)(kt_ + row_b * kHeadDim);
-        if (VROWS) {  // V as rows: its tile is staged exactly like K's
-            const half_t* vt_ = Vp + (size_t)(j * kTile) * kHeadDim + cc * 8;
-            va = *(const uint4*)(vt_ + row_a * kHeadDim);
-            vb = *(const uint4*)(vt_ + row_b * kHeadDim);
-        } else {
-            va = *(const uint4*)(Vp + (size_t)row_a * T + j * kTile + cc * 8);
-            vb = *(const uint4*)(Vp + (size_t)row_b * T + j * kTile + cc * 8);
-        }
+        const int ktile = j * kTile * kHeadDim * 2, vtile = VROWS ? ktile : j * kTile * 2;
+        ka = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, k_off_a, ktile, 0));
+        kb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, k_off_b, ktile, 0));
+        va = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(v_rsrc, v_off_a, vtile, 0));
+        vb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(v_rsrc, v_off_b, vtile, 0));
     };
     auto store = [&](int j, int kbuf, int buf, uint4 ka, uint4 kb, uint4 va, uint4 vb) {
         if (VARLEN) {
