@@ -88,7 +88,11 @@ __global__ __launch_bounds__(kRowThreads) void sa_row_terms_kernel(const half_t*
 // ---------------------------------------------------------------------------
 constexpr int kSubRows = 32;
 constexpr int kSubBytes = kSubRows * kHeadDim * 2;          // 4096
-constexpr int kItemBytes = 2 * kSubBytes + 2 * kSubRows * 4;  // Q, dO, L, D: 8448
+// Q, dO, then two 256-byte blocks: L in the first's lanes 0..31, D in the
+// second's lanes 32..63 (each written by a 64-lane load whose other lanes
+// fall outside its resource).
+constexpr int kItemBytes = 2 * kSubBytes + 2 * 64 * 4;          // 8704
+constexpr int kDOffsetFloats = 64 + 32;                          // D block, lane 32
 constexpr int kWaveBytes = 2 * kItemBytes;
 constexpr int kRedRow = 68;                                  // floats
 
@@ -139,8 +143,9 @@ __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t vof
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)((__attribute__((address_space(3))) char*)lds_wave_base),
                                              16, voffset, 0, OFF, 0);
 }
-__device__ __forceinline__ void dma4(const void* g, char* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)((__attribute__((address_space(3))) char*)lds_wave_base), 4, 0, 0);
+__device__ __forceinline__ void dma4_buf(__amdgpu_buffer_rsrc_t r, uint32_t voffset, char* lds_wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)((__attribute__((address_space(3))) char*)lds_wave_base),
+                                             4, voffset, 0, 0, 0);
 }
 
 template <bool CAUSAL, bool VARLEN, int GW>
@@ -219,14 +224,17 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     const int dma_row = lane >> 3;                         // + 8 u
     // Direct loads of one item into buffer `buf`: 4 x 1 KB of Q rows, 4 x 1 KB
     // of dO rows (lane l of load u: row 8 u + l / 8, stored chunk l % 8 holding
-    // the row's chunk (l % 8) ^ swz_key(row)), then L (lanes 0..31) and D (32..63).
+    // the row's chunk (l % 8) ^ swz_key(row)), then L into the first 256-byte
+    // block (lanes 0..31) and D into the second (lanes 32..63).
     // Row 16 u + r has the chunk permutation of row r, so loads u and u + 2
     // differ by 2 KB in memory and in LDS: the instruction's offset field.
     const uint32_t dma_off0 = (uint32_t)(dma_row * kHeadDim + ((lane & 7) ^ swz_key(dma_row)) * 8) * 2u;
     const uint32_t dma_off1 = (uint32_t)(dma_row * kHeadDim + ((lane & 7) ^ swz_key(dma_row + 8)) * 8) * 2u;
-    // The item's Q and dO rows as buffer resources built on the scalar unit:
-    // their loads take the fixed per-lane offsets, so no vector instruction
-    // forms their addresses.
+    // The item's rows as buffer resources built on the scalar unit: the loads
+    // take fixed per-lane offsets, so no vector instruction forms an address.
+    // L's and D's resources hold the item's 32 values each; the other 32 lanes
+    // of their 64-lane loads fall outside and fill unused slots with zeros.
+    const uint32_t ld_off_l = 4u * (uint32_t)lane, ld_off_d = 4u * (uint32_t)lane - 128u;
     auto issue_item = [&](int head, int sub, int buf) {
         const size_t rowbase = ((size_t)b * H + head) * T + (size_t)sub * kSubRows;
         const __amdgpu_buffer_rsrc_t qr =
@@ -242,8 +250,10 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
         dma16_buf<1024>(orr, dma_off1, base + kSubBytes);
         dma16_buf<2048>(orr, dma_off0, base + kSubBytes);
         dma16_buf<3072>(orr, dma_off1, base + kSubBytes);
-        const float* src = (lane < 32) ? (L + rowbase + lane) : (D + rowbase + (lane - 32));
-        dma4(src, base + 2 * kSubBytes);
+        dma4_buf(__builtin_amdgcn_make_buffer_rsrc((void*)(L + rowbase), (short)0, kSubRows * 4, kBufferRsrcWord3),
+                 ld_off_l, base + 2 * kSubBytes);
+        dma4_buf(__builtin_amdgcn_make_buffer_rsrc((void*)(D + rowbase), (short)0, kSubRows * 4, kBufferRsrcWord3),
+                 ld_off_d, base + 2 * kSubBytes + 256);
     };
 
     // Items in order: for each of the slot's heads, sub-tiles from the last down.
@@ -327,7 +337,7 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
         half_t* Qs = (half_t*)(wstage + buf * kItemBytes);
         half_t* dOs = Qs + kSubRows * kHeadDim;
         float* Ls = (float*)(dOs + kSubRows * kHeadDim);
-        const float* Ds = Ls + kSubRows;
+        float* Ds = Ls + kDOffsetFloats;
         if (VARLEN && qb + kSubRows > len) {
             // Rows at or past the length never reach dK or dV: clear them.
             const int keep = max(len - qb, 0);
@@ -339,7 +349,7 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
                     *(uint4*)(dOs + row * kHeadDim + (lane & 7) * 8) = make_uint4(0, 0, 0, 0);
                 }
             }
-            if ((lane & 31) >= keep) Ls[lane] = 0.0f;  // L (lanes 0..31) and D (32..63)
+            if ((lane & 31) >= keep) (lane < 32 ? Ls : Ds)[lane & 31] = 0.0f;
         }
         // The previous item's transposed operands; once they are in registers
         // its buffer takes the next item.
