@@ -203,3 +203,26 @@ def test_row_terms_from_the_forward_output():
     want = np.sum(x["dO"].astype(np.float64) * O16, axis=-1)
     want[1, :, 77:] = 0.0
     assert np.max(np.abs(got["D"] - want)) <= 1e-5 * max(1.0, np.max(np.abs(want)))
+
+
+def test_long_sequence_t65536_sampled():
+    """T = 65536 with two query heads on one K/V head: the dS workspace alone
+    is 8.6 GB, and every in-kernel offset and buffer-resource size is 4x the
+    long-context workload's.  Sampled rows (tile edges included) and the last
+    1024 key columns against the oracle."""
+    T, H, KV = 65536, 2, 1
+    say(f"case long_causal_t{T}")
+    x = make_inputs(1, T, H, KV, seed=31)
+    _, got = run_gpu(x, True)
+    rows = sample_rows(1, H, T, 96, seed=31)
+    say(f"case long_causal_t{T}: oracle rows {rows.size}")
+    D, dQ, O, L = oracle.backward_rows(x["Q"], x["K"], x["Vt"], x["dO"], s=SCALE, causal=True, seqlens=None,
+                                       rows=rows)
+    check_forward(got["O"].reshape(-1, 64)[rows], got["L"].reshape(-1)[rows], O, L, "t65536")
+    check_grad("dQ", got["dQ"].reshape(-1, 64)[rows], dQ, "t65536")
+    assert rel_l2(got["D"].reshape(-1)[rows], D) <= 1e-2
+    cols = sample_cols(1, KV, T, 48, seed=32, lo=T - 1024)
+    say(f"case long_causal_t{T}: oracle cols {cols.size}")
+    dK, dV = oracle.backward_cols(x["Q"], x["K"], x["Vt"], x["dO"], s=SCALE, causal=True, seqlens=None, cols=cols)
+    check_grad("dK", got["dK"].reshape(-1, 64)[cols], dK, "t65536")
+    check_grad("dV", np.swapaxes(got["dVt"], -1, -2).reshape(-1, 64)[cols], dV, "t65536")
