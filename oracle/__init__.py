@@ -15,7 +15,12 @@ the pages, is stated in ``sa_oracle.c``:
 * backward rows and key columns: same page, banner "The backward pass,
   deterministic and in two launches" (D, dP, dS, dQ, dK, dV);
 * length masks and zero output for fully masked rows: the variable-length
-  gist page (``self_attn_fwd``).
+  gist page (``self_attn_fwd``);
+* ``rotated_dq_slice`` (plain numpy, binary64): dQ turned back by the inverse
+  half-split rotation and laid out as the Q slice of a token-major projection
+  gradient, as the same page's query pass stores it in its rotated variant
+  (the "dQ = s (the sum), turned back by the inverse half-split rotation"
+  epilogue).
 
 Array layouts follow the library: Q, dO ``[B][H][T][64]``; K ``[B][KV][T][64]``;
 Vt ``[B][KV][64][T]``; the outputs are float64.  Inputs may be float16 (the
@@ -165,3 +170,26 @@ def backward(Q, K, Vt, dO, *, s, causal, seqlens=None):
         "dQ": dQ.reshape(B, H, T, 64), "dK": dK.reshape(B, KV, T, 64),
         "dVt": dV.reshape(B, KV, T, 64).transpose(0, 1, 3, 2).copy(),
     }
+
+
+def rotated_dq_slice(dQ, cos, sin, width):
+    """The Q slice of a token-major projection gradient [B][T][width] (binary64).
+
+    StreamingAttentionSM86 page, the query pass's rotated epilogue: dQ
+    [B][H][T][64] (already scaled by s) is turned back by the inverse of the
+    half-split rotation, whose tables cos and sin are [T][32] (position p,
+    column pair c < 32), and row p, column c of head h lands at (p, 64 h + c):
+        out[64 h + c]      = dQ[c] cos[p][c] + dQ[c + 32] sin[p][c]
+        out[64 h + c + 32] = dQ[c + 32] cos[p][c] - dQ[c] sin[p][c]
+    Columns at or past 64 H are zero here (the library leaves them untouched).
+    """
+    dQ = np.asarray(dQ, dtype=np.float64)
+    B, H, T, d = dQ.shape
+    assert d == 64 and width >= 64 * H
+    c = np.asarray(cos, dtype=np.float64)[None, None, :, :]   # [1,1,T,32]
+    s_ = np.asarray(sin, dtype=np.float64)[None, None, :, :]
+    x1, x2 = dQ[..., :32], dQ[..., 32:]
+    rot = np.concatenate([x1 * c + x2 * s_, x2 * c - x1 * s_], axis=-1)   # [B,H,T,64]
+    out = np.zeros((B, T, width))
+    out[:, :, :64 * H] = rot.transpose(0, 2, 1, 3).reshape(B, T, 64 * H)
+    return out

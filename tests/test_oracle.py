@@ -250,3 +250,50 @@ def test_oracle_rejects_bad_ids_and_shapes():
         oracle.forward_rows(x["Q"], x["K"], x["Vt"], s=SCALE, causal=True, rows=[128])
     with pytest.raises(ValueError):
         oracle.forward(x["Q"], x["K"][:, :, :32], x["Vt"], s=SCALE, causal=True)
+
+
+# --- the rotated dQ slice (inverse half-split rotation, projection layout) ---
+
+def _half_split_rotate(q, cos, sin):
+    """The forward half-split rotation of query rows q [..., T, 64] by angle tables [T, 32]:
+    each column pair (c, c + 32) is the 2-vector (x, y) turned by the angle: (x cos - y sin, x sin + y cos)."""
+    x, y = q[..., :32], q[..., 32:]
+    return np.concatenate([x * cos - y * sin, x * sin + y * cos], axis=-1)
+
+
+def _angles(T, seed):
+    rng = np.random.default_rng(seed)
+    theta = rng.uniform(-np.pi, np.pi, size=(T, 32))
+    return np.cos(theta), np.sin(theta)
+
+
+def test_rotated_slice_is_the_adjoint_of_the_rotation():
+    """<rotate(q), g> = <q, inverse(g)> for every q: the slice holds the gradient with respect to the
+    unrotated queries, given the gradient g with respect to the rotated ones."""
+    B, H, T = 2, 3, 16
+    rng = np.random.default_rng(5)
+    cos, sin = _angles(T, 6)
+    q = rng.standard_normal((B, H, T, 64))
+    g = rng.standard_normal((B, H, T, 64))
+    lhs = np.sum(_half_split_rotate(q, cos, sin) * g, axis=-1)          # [B,H,T]
+    out = oracle.rotated_dq_slice(g, cos, sin, width=64 * H)
+    inv = out.reshape(B, T, H, 64).transpose(0, 2, 1, 3)
+    rhs = np.sum(q * inv, axis=-1)
+    assert np.allclose(lhs, rhs, rtol=0, atol=1e-12)
+    # and turning the slice forward again gives g back (the rotation is orthogonal)
+    assert np.allclose(_half_split_rotate(inv, cos, sin), g, rtol=0, atol=1e-12)
+
+
+def test_rotated_slice_special_angles_and_layout():
+    B, H, T, W = 1, 2, 8, 3 * 64
+    rng = np.random.default_rng(7)
+    g = rng.standard_normal((B, H, T, 64))
+    one, zero = np.ones((T, 32)), np.zeros((T, 32))
+    ident = oracle.rotated_dq_slice(g, one, zero, width=W)        # angle 0: plain placement
+    for h in range(H):
+        assert np.array_equal(ident[0, :, 64 * h:64 * h + 64], g[0, h])
+    assert np.all(ident[:, :, 64 * H:] == 0.0)
+    quarter = oracle.rotated_dq_slice(g, zero, one, width=W)      # angle pi/2: (x, y) -> (y, -x)
+    for h in range(H):
+        assert np.array_equal(quarter[0, :, 64 * h:64 * h + 32], g[0, h, :, 32:])
+        assert np.array_equal(quarter[0, :, 64 * h + 32:64 * h + 64], -g[0, h, :, :32])
