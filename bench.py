@@ -438,6 +438,31 @@ def main():
                   "note": "the same step with V as rows [KV][T][64] (no transposed copy of V) and dV returned "
                           "as rows; bitwise-identical outputs"}
 
+    # The dQ pass with the rotated epilogue (dQ turned back by the inverse
+    # half-split rotation into a bfloat16 [T][width] projection gradient), on
+    # the headline's stored dS, timed alone beside the plain dQ pass.
+    dq_rotated = None
+    if not args.headline_only:
+        width = (w.heads + 2 * w.kv_heads) * HEAD_DIM
+        theta = torch.rand(w.T, 32, device="cuda", dtype=torch.float32) * 6.2831855
+        cos_t, sin_t = torch.cos(theta).contiguous(), torch.sin(theta).contiguous()
+        dqkv = torch.zeros(w.batch, w.T, width, dtype=torch.int16, device="cuda")
+        rot_args = (sh, buf.K, buf.dS, buf.ws_bytes, SCALE, cos_t, sin_t, dqkv, width, stream)
+        for _ in range(args.warmup):
+            sa.sa_dq_pass_rotated(*rot_args)
+        ra, rb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ra.record(stream)
+        for _ in range(args.steps):
+            sa.sa_dq_pass_rotated(*rot_args)
+        rb.record(stream)
+        torch.cuda.synchronize()
+        rot_ms = ra.elapsed_time(rb) / args.steps
+        dq_rotated = {"ms": round(rot_ms, 4), "tflops": round(fl["dq_pass"] / (rot_ms * 1e-3) / 1e12, 1),
+                      "projection_width": width,
+                      "note": "sa_dq_pass_rotated alone, back to back: dQ turned back by the inverse half-split "
+                              "rotation and stored as the bfloat16 Q slice of a token-major [T][width] gradient"}
+
     if args.calibrate_copy_mb > 0:
         n = args.calibrate_copy_mb << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -466,6 +491,8 @@ def main():
         out["two_pass_backward"] = two_pass
     if v_rows is not None:
         out["v_rows"] = v_rows
+    if dq_rotated is not None:
+        out["dq_pass_rotated"] = dq_rotated
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x)
     print(json.dumps(out), flush=True)

@@ -54,6 +54,7 @@ _SIGS = {
     "sa_row_terms": (_I, [_SP, _V, _V, _V, _V]),
     "sa_key_pass": (_I, [_SP, _V, _V, _V, _V, _V, _V, _V, _Z, _F, _F, _V, _V, _V]),
     "sa_dq_pass": (_I, [_SP, _V, _V, _Z, _F, _V, _V]),
+    "sa_dq_pass_rotated": (_I, [_SP, _V, _V, _Z, _F, _V, _V, _V, _I, _V]),
     "sa_query_pass": (_I, [_SP, _V, _V, _V, _V, _V, _V, _F, _F, _V, _V, _V]),
     "sa_backward_two_pass": (_I, [_SP, _V, _V, _V, _V, _V, _V, _V, _F, _F, _V, _V, _V, _V]),
     "sa_status_string": (ctypes.c_char_p, [_I]),
@@ -164,6 +165,11 @@ def sa_key_pass(shape, Q, K, Vt, dO, L, D, dS, dS_bytes, c, s, dK, dVt, stream=N
 def sa_dq_pass(shape, K, dS, dS_bytes, s, dQ, stream=None):
     _check(native().sa_dq_pass(ctypes.byref(shape), _ptr(K), _ptr(dS), dS_bytes, s, _ptr(dQ),
                                _stream(stream)), "sa_dq_pass")
+
+
+def sa_dq_pass_rotated(shape, K, dS, dS_bytes, s, cos, sin, dqkv, width, stream=None):
+    _check(native().sa_dq_pass_rotated(ctypes.byref(shape), _ptr(K), _ptr(dS), dS_bytes, s, _ptr(cos), _ptr(sin),
+                                       _ptr(dqkv), width, _stream(stream)), "sa_dq_pass_rotated")
 
 
 def sa_query_pass(shape, dO, O, L, Q, K, Vt, c, s, D, dQ, stream=None):

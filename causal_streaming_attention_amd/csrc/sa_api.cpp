@@ -126,6 +126,18 @@ sa_status sa_dq_pass(const sa_shape* shape, const void* K, const void* dS, size_
     return from_hip(sa::launch_dq_pass(to_shape(shape), K, dS, s, dQ, (hipStream_t)stream));
 }
 
+sa_status sa_dq_pass_rotated(const sa_shape* shape, const void* K, const void* dS, size_t dS_bytes, float s,
+                             const float* cos_t, const float* sin_t, void* dqkv, int width, void* stream) {
+    sa_status st = sa_check_shape(shape);
+    if (st != SA_OK) return st;
+    if ((st = check_ptrs({K, dS, cos_t, sin_t, dqkv})) != SA_OK) return st;
+    if (dS_bytes < sa_backward_workspace_bytes(shape)) return SA_ERR_WORKSPACE;
+    if (!scale_ok(s)) return SA_ERR_ARGUMENT;
+    if (width % 8 != 0 || (long long)width < 64ll * shape->heads) return SA_ERR_ARGUMENT;
+    return from_hip(sa::launch_dq_pass_rotated(to_shape(shape), K, dS, s, cos_t, sin_t, dqkv, width,
+                                               (hipStream_t)stream));
+}
+
 sa_status sa_backward_ex(const sa_shape* shape, const void* dO, const void* O, const float* L, float* D, void* dS,
                          size_t dS_bytes, const void* Q, const void* K, const void* Vt, float c, float s,
                          float* dQ, float* dK, float* dVt, void* stream) {
@@ -177,7 +189,7 @@ const char* sa_status_string(int status) {
         case SA_ERR_NULL: return "a required pointer is NULL";
         case SA_ERR_ALIGN: return "a pointer is not 16-byte aligned (seqlens: 4-byte)";
         case SA_ERR_WORKSPACE: return "dS workspace smaller than sa_backward_workspace_bytes";
-        case SA_ERR_ARGUMENT: return "scale c or s is not finite and positive";
+        case SA_ERR_ARGUMENT: return "scale c or s is not finite and positive, or a bad projection width";
         case SA_ERR_DEVICE: return "a HIP kernel launch failed";
         default: return "unknown status";
     }

@@ -516,13 +516,32 @@ constexpr int kDqVmPerStep = 2 + 4;               // per lane: K DMA, dS loads
 constexpr int kDqKWait = 4 + (kDqLead - 1) * kDqVmPerStep;
 static_assert(kDqKWait == 22, "the s_waitcnt immediate below");
 
-template <bool CAUSAL, bool VARLEN>
+// Round to nearest even bfloat16: the upper half of the binary32 word after
+// adding half an ulp of the kept part, ties going to the even one (inputs are
+// finite).
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
+    return make_uint2(bf16_bits(a) | (bf16_bits(b) << 16), bf16_bits(c) | (bf16_bits(d) << 16));
+}
+
+// ROT: the epilogue of the query pass's rotated variant (StreamingAttentionSM86
+// page, "dQ = s (the sum), turned back by the inverse half-split rotation"):
+// the scaled pair (x1, x2) of columns c and c + 32 at position p becomes
+// (x1 cos + x2 sin, x2 cos - x1 sin) with the [T][32] tables' entry (p, c),
+// each product rounded as the page's FMUL then FFMA, and is stored as
+// bfloat16 at columns 64 h + c and 64 h + c + 32 of row p of the token-major
+// [B][T][width] projection gradient; dQ itself is not written.
+template <bool CAUSAL, bool VARLEN, bool ROT>
 __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __restrict__ K,
                                                                const half_t* __restrict__ dS,
                                                                float* __restrict__ dQ,
                                                                const int32_t* __restrict__ seqlens, float s,
                                                                int T, int H, int KV, int n_qblk, int BH,
-                                                               int block_order, long long tiles_per_head) {
+                                                               int block_order, long long tiles_per_head,
+                                                               DqRotation rot) {
     __shared__ __attribute__((aligned(16))) half_t lds[kDqDepth][kKTileHalves];  // K tiles
     __shared__ __attribute__((aligned(16))) half_t dsl[kDqWaves][kDsBlockHalves];  // each wave's dS block
 
@@ -700,8 +719,29 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
             step(kt + 4, sl4, sl3);
         }
         if (!wave_rows) return;
-        float* dq = dQ + (((size_t)b * H + h) * T + q) * kHeadDim;
         const float scale = (!VARLEN || q < len) ? s : 0.0f;
+        if (ROT) {
+            // Each lane holds columns c = 8 rg + 4 hi + 0..3 and c + 32 of its query's row.
+            const float* cr = rot.cos + (size_t)q * 32;
+            const float* sr = rot.sin + (size_t)q * 32;
+            uint16_t* orow = rot.out + ((size_t)b * T + q) * (size_t)rot.width + kHeadDim * h;
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int c0 = 8 * rg + 4 * hi;
+                const f32x4 cv = *(const f32x4*)(cr + c0), sv = *(const f32x4*)(sr + c0);
+                float o1[4], o2[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float x1 = acc0[4 * rg + i] * scale, x2 = acc1[4 * rg + i] * scale;
+                    o1[i] = __builtin_fmaf(x1, cv[i], x2 * sv[i]);
+                    o2[i] = __builtin_fmaf(x2, cv[i], -(x1 * sv[i]));
+                }
+                *(uint2*)(orow + c0) = pack_bf16x4(o1[0], o1[1], o1[2], o1[3]);
+                *(uint2*)(orow + 32 + c0) = pack_bf16x4(o2[0], o2[1], o2[2], o2[3]);
+            }
+            return;
+        }
+        float* dq = dQ + (((size_t)b * H + h) * T + q) * kHeadDim;
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
             f32x4 v0 = {acc0[4 * rg], acc0[4 * rg + 1], acc0[4 * rg + 2], acc0[4 * rg + 3]};
@@ -795,21 +835,32 @@ hipError_t launch_key_pass(const Shape& sh, const void* Q, const void* K, const 
     return hipGetLastError();
 }
 
-hipError_t launch_dq_pass(const Shape& sh, const void* K, const void* dS, float s, float* dQ,
-                          hipStream_t stream) {
+template <bool ROT>
+hipError_t launch_dq(const Shape& sh, const void* K, const void* dS, float s, float* dQ, const DqRotation& rot,
+                     hipStream_t stream) {
     const int n_qblk = (sh.T + kDqRows - 1) / kDqRows, BH = sh.batch * sh.heads;
     dim3 grid((unsigned)dq_pass_blocks(sh)), block(kDqThreads);
     const long long tph = (long long)ds_tiles_per_head(sh);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, stream, (const half_t*)K, (const half_t*)dS, dQ, sh.seqlens, s,
-                           sh.T, sh.heads, sh.kv_heads, n_qblk, BH, sh.block_order, tph);
+                           sh.T, sh.heads, sh.kv_heads, n_qblk, BH, sh.block_order, tph, rot);
     };
     if (sh.causal) {
-        if (sh.seqlens) go(sa_dq_kernel<true, true>); else go(sa_dq_kernel<true, false>);
+        if (sh.seqlens) go(sa_dq_kernel<true, true, ROT>); else go(sa_dq_kernel<true, false, ROT>);
     } else {
-        if (sh.seqlens) go(sa_dq_kernel<false, true>); else go(sa_dq_kernel<false, false>);
+        if (sh.seqlens) go(sa_dq_kernel<false, true, ROT>); else go(sa_dq_kernel<false, false, ROT>);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_dq_pass(const Shape& sh, const void* K, const void* dS, float s, float* dQ,
+                          hipStream_t stream) {
+    return launch_dq<false>(sh, K, dS, s, dQ, DqRotation{nullptr, nullptr, nullptr, 0}, stream);
+}
+
+hipError_t launch_dq_pass_rotated(const Shape& sh, const void* K, const void* dS, float s, const float* cos_t,
+                                  const float* sin_t, void* dqkv, int width, hipStream_t stream) {
+    return launch_dq<true>(sh, K, dS, s, nullptr, DqRotation{cos_t, sin_t, (uint16_t*)dqkv, width}, stream);
 }
 
 }  // namespace sa

@@ -31,6 +31,17 @@ hipError_t launch_key_pass(const Shape& sh, const void* Q, const void* K, const 
                            hipStream_t stream);
 hipError_t launch_dq_pass(const Shape& sh, const void* K, const void* dS, float s, float* dQ,
                           hipStream_t stream);
+// The dQ pass with the rotated epilogue: dQ turned back by the inverse
+// half-split rotation (tables cos_t, sin_t fp32 [T][32]) and stored as the
+// bfloat16 Q slice of the token-major projection gradient dqkv [B][T][width].
+struct DqRotation {
+    const float* cos;
+    const float* sin;
+    uint16_t* out;
+    int width;
+};
+hipError_t launch_dq_pass_rotated(const Shape& sh, const void* K, const void* dS, float s, const float* cos_t,
+                                  const float* sin_t, void* dqkv, int width, hipStream_t stream);
 // The two-launch backward's query pass (D and dQ); its key launch is
 // launch_key_pass with dS == nullptr (no score gradients stored).
 hipError_t launch_query_pass(const Shape& sh, const void* dO, const void* O, const float* L, const void* Q,

@@ -179,6 +179,30 @@ sa_status sa_dq_pass(const sa_shape* shape, const void* K, const void* dS, size_
                      float* dQ, void* stream);
 
 /*
+ * The dQ pass with the rotated epilogue (StreamingAttentionSM86 page, the
+ * query pass's "dQ = s (the sum), turned back by the inverse half-split
+ * rotation" epilogue, dQ from stored dS): dQ is formed as by sa_dq_pass, and
+ * each scaled pair (x1, x2) of columns c and c + 32 (c < 32) of row p of head
+ * h becomes (x1 cos + x2 sin, x2 cos - x1 sin), with cos = cos_t[p][c] and
+ * sin = sin_t[p][c], rounded to bfloat16 (nearest even) and stored at columns
+ * 64 h + c and 64 h + c + 32 of row p of the token-major projection gradient.
+ * This is the gradient with respect to the queries before the half-split
+ * rotation, laid out as the Q slice of a fused QKV projection's gradient.
+ *   cos_t, sin_t: fp32 [T][32], the rotation's tables (shared by the batch
+ *                 and the heads), 16-byte aligned.
+ *   dqkv:         bf16 [B][T][width]; columns 0 .. 64 heads - 1 of every row
+ *                 are overwritten (zeros on padded rows), every other column
+ *                 is left untouched.
+ *   width:        row length of dqkv in elements: a multiple of 8 and at
+ *                 least 64 heads (else SA_ERR_ARGUMENT).
+ * dQ itself is not written.  The page's admission also asks for a power-of-
+ * two sequence and 32-bit byte offsets; neither is needed here (64-bit
+ * addressing, no shift-based indexing).
+ */
+sa_status sa_dq_pass_rotated(const sa_shape* shape, const void* K, const void* dS, size_t dS_bytes, float s,
+                             const float* cos_t, const float* sin_t, void* dqkv, int width, void* stream);
+
+/*
  * The backward in two launches, with no dS workspace (StreamingAttentionSM86
  * page, banner "The backward pass, deterministic and in two launches (no
  * atomics)"): the query launch forms D and dQ, recomputing S, P and dP per

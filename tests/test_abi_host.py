@@ -192,3 +192,24 @@ def test_base2_scale_is_the_nearest_binary32():
     import struct
     c = sa.base2_scale(0.125)
     assert struct.pack(">f", c).hex() == "3e38aa3b"
+
+
+def test_rotated_dq_pass_rejects_bad_arguments(lib):
+    s = shape()
+    need = sa.sa_backward_workspace_bytes(s)
+    W = 64 * s.heads
+
+    def call(p, ws=need, sc=0.125, width=W):
+        return lib.sa_dq_pass_rotated(ctypes.byref(s), p[0], p[1], ws, sc, p[2], p[3], p[4], width, None)
+
+    ptrs = [FAKE] * 5   # K dS cos sin dqkv
+    for i in range(5):
+        bad = list(ptrs)
+        bad[i] = None
+        assert call(bad) == sa.SA_ERR_NULL
+        bad[i] = FAKE + 8
+        assert call(bad) == sa.SA_ERR_ALIGN
+    assert call(ptrs, ws=need - 1) == sa.SA_ERR_WORKSPACE
+    assert call(ptrs, sc=float("inf")) == sa.SA_ERR_ARGUMENT
+    assert call(ptrs, width=W - 8) == sa.SA_ERR_ARGUMENT      # narrower than the Q slice
+    assert call(ptrs, width=W + 4) == sa.SA_ERR_ARGUMENT      # not a multiple of 8
