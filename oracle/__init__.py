@@ -20,7 +20,10 @@ the pages, is stated in ``sa_oracle.c``:
   half-split rotation and laid out as the Q slice of a token-major projection
   gradient, as the same page's query pass stores it in its rotated variant
   (the "dQ = s (the sum), turned back by the inverse half-split rotation"
-  epilogue).
+  epilogue);
+* ``projection_slices`` (plain numpy): dQ, dK and dV laid out as the Q, K and
+  V column slices of a fused projection's token-major gradient, as the same
+  page's query and key launches store them in their projection variants.
 
 Array layouts follow the library: Q, dO ``[B][H][T][64]``; K ``[B][KV][T][64]``;
 Vt ``[B][KV][64][T]``; the outputs are float64.  Inputs may be float16 (the
@@ -192,4 +195,20 @@ def rotated_dq_slice(dQ, cos, sin, width):
     rot = np.concatenate([x1 * c + x2 * s_, x2 * c - x1 * s_], axis=-1)   # [B,H,T,64]
     out = np.zeros((B, T, width))
     out[:, :, :64 * H] = rot.transpose(0, 2, 1, 3).reshape(B, T, 64 * H)
+    return out
+
+
+def projection_slices(dQ, dK, dVt, width, q_col, k_col, v_col):
+    """dQ [B][H][T][64], dK [B][KV][T][64] and dVt [B][KV][64][T] laid out in one token-major [B][T][width]
+    gradient (binary64): row t holds head h's dQ at columns q_col + 64 h + c, K/V head kv's dK at
+    k_col + 64 kv + c and dV at v_col + 64 kv + c (StreamingAttentionSM86 page, the query and key launches'
+    projection epilogues: dQ, dK and dV "stored straight into a fused projection's gradient").  Other
+    columns are zero."""
+    dQ, dK, dVt = (np.asarray(a, dtype=np.float64) for a in (dQ, dK, dVt))
+    B, H, T, _ = dQ.shape
+    KV = dK.shape[1]
+    out = np.zeros((B, T, width))
+    out[:, :, q_col:q_col + 64 * H] = dQ.transpose(0, 2, 1, 3).reshape(B, T, 64 * H)
+    out[:, :, k_col:k_col + 64 * KV] = dK.transpose(0, 2, 1, 3).reshape(B, T, 64 * KV)
+    out[:, :, v_col:v_col + 64 * KV] = dVt.transpose(0, 3, 1, 2).reshape(B, T, 64 * KV)
     return out

@@ -297,3 +297,36 @@ def test_rotated_slice_special_angles_and_layout():
     for h in range(H):
         assert np.array_equal(quarter[0, :, 64 * h:64 * h + 32], g[0, h, :, 32:])
         assert np.array_equal(quarter[0, :, 64 * h + 32:64 * h + 64], -g[0, h, :, :32])
+
+
+def test_projection_slices_give_the_fused_projection_input_gradient():
+    """End to end through a real fused QKV projection: with Q, K, V = slices of X W (X [T][n], W [n][width]),
+    attention (torch binary64, GQA by repeated heads) and a loss sum(O * dO), autograd's dX equals G W^T
+    where G is the oracle's gradients laid out by projection_slices."""
+    B, T, H, KV, n = 1, 64, 4, 2, 24
+    G_ = H // KV
+    width = 64 * (H + 2 * KV)
+    q_col, k_col, v_col = 0, 64 * H, 64 * (H + KV)
+    rng = np.random.default_rng(11)
+    X = rng.standard_normal((T, n)) * 0.5
+    W = rng.standard_normal((n, width)) * 0.3
+    # the projected inputs, rounded to binary16 as the library takes them
+    P = (X @ W).astype(np.float16).astype(np.float64)
+    Q = P[:, q_col:q_col + 64 * H].reshape(T, H, 64).transpose(1, 0, 2)[None]
+    K = P[:, k_col:k_col + 64 * KV].reshape(T, KV, 64).transpose(1, 0, 2)[None]
+    V = P[:, v_col:v_col + 64 * KV].reshape(T, KV, 64).transpose(1, 0, 2)[None]
+    dO = rng.standard_normal((B, H, T, 64))
+    ref = oracle.backward(Q, K, np.ascontiguousarray(V.transpose(0, 1, 3, 2)), dO, s=SCALE, causal=True)
+    Gm = oracle.projection_slices(ref["dQ"], ref["dK"], ref["dVt"], width, q_col, k_col, v_col)[0]
+    # autograd: the same attention on the projected (unrounded-through-autograd) values
+    Xt = torch.tensor(X, requires_grad=True)
+    Pt = Xt @ torch.tensor(W)
+    Pt = Pt + (torch.tensor(P) - Pt).detach()          # forward values = the binary16-rounded ones
+    qt = Pt[:, q_col:q_col + 64 * H].reshape(T, H, 64).transpose(0, 1)[None]
+    kt = Pt[:, k_col:k_col + 64 * KV].reshape(T, KV, 64).transpose(0, 1)[None].repeat_interleave(G_, dim=1)
+    vt = Pt[:, v_col:v_col + 64 * KV].reshape(T, KV, 64).transpose(0, 1)[None].repeat_interleave(G_, dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=SCALE)
+    (o * torch.tensor(dO)).sum().backward()
+    want = Xt.grad.numpy()
+    got = Gm @ W.T
+    assert np.max(np.abs(got - want)) <= 1e-9 * max(1.0, np.max(np.abs(want)))
