@@ -138,6 +138,26 @@ sa_status sa_dq_pass_rotated(const sa_shape* shape, const void* K, const void* d
                                                (hipStream_t)stream));
 }
 
+sa_status sa_backward_projection(const sa_shape* shape, const void* dO, const void* O, const float* L, float* D,
+                                 void* dS, size_t dS_bytes, const void* Q, const void* K, const void* Vt,
+                                 float c, float s, float* dQ32, void* dQ16, float* dK32, void* dK16,
+                                 float* dV32, void* dV16, int width, void* stream) {
+    sa_status st = sa_check_shape(shape);
+    if (st != SA_OK) return st;
+    if ((st = check_ptrs({dO, O, L, D, dS, Q, K, Vt, dQ32, dQ16, dK32, dK16, dV32, dV16})) != SA_OK) return st;
+    if (dS_bytes < sa_backward_workspace_bytes(shape)) return SA_ERR_WORKSPACE;
+    if (!scale_ok(c) || !scale_ok(s)) return SA_ERR_ARGUMENT;
+    if (width % 8 != 0 || (long long)width < 64ll * shape->heads) return SA_ERR_ARGUMENT;
+    const sa::Shape sh = to_shape(shape);
+    hipStream_t strm = (hipStream_t)stream;
+    const sa::ProjectionOut q{dQ32, (uint16_t*)dQ16, width}, k{dK32, (uint16_t*)dK16, width},
+        v{dV32, (uint16_t*)dV16, width};
+    if ((st = from_hip(sa::launch_row_terms(sh, dO, O, D, strm))) != SA_OK) return st;
+    if ((st = from_hip(sa::launch_key_pass_projection(sh, Q, K, Vt, dO, L, D, dS, c, s, k, v, strm))) != SA_OK)
+        return st;
+    return from_hip(sa::launch_dq_pass_projection(sh, K, dS, s, q, strm));
+}
+
 sa_status sa_backward_ex(const sa_shape* shape, const void* dO, const void* O, const float* L, float* D, void* dS,
                          size_t dS_bytes, const void* Q, const void* K, const void* Vt, float c, float s,
                          float* dQ, float* dK, float* dVt, void* stream) {

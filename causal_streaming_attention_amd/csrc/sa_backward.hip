@@ -24,6 +24,18 @@ namespace sa {
 
 namespace {
 
+// Round to nearest even bfloat16: the upper half of the binary32 word after
+// adding half an ulp of the kept part, ties going to the even one (inputs are
+// finite).
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
+    return make_uint2(bf16_bits(a) | (bf16_bits(b) << 16), bf16_bits(c) | (bf16_bits(d) << 16));
+}
+
+
 // ---------------------------------------------------------------------------
 // Row terms: D[b][h][i] = sum_d dO[b][h][i][d] * O[b][i][h*64 + d] in binary32
 // (each fp16 widened, fused multiply-adds), 0 on padded rows.  Eight lanes
@@ -154,7 +166,7 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     const half_t* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ D,
     half_t* __restrict__ dS, float* __restrict__ dK, float* __restrict__ dVt,
     const int32_t* __restrict__ seqlens, float c, float s, int T, int H, int KV, int nkt, int BKV,
-    int block_order, long long tiles_per_head, int v_rows) {
+    int block_order, long long tiles_per_head, int v_rows, ProjectionOut kproj, ProjectionOut vproj) {
     constexpr int kThreads = 128 * GW;
     __shared__ __attribute__((aligned(16))) char smem[KeyLds<GW>::bytes];
 
@@ -442,6 +454,17 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
             *(f32x4*)(row + 32) = v1;
         }
     };
+    // Projection variant (same page, the key launch's "dK = s (the sum) and dV
+    // stored straight into a fused projection's gradient"): row p of the
+    // token-major gradient takes K/V head kv's values at columns 64 kv + d of
+    // the slice the pointers name, in binary32 and rounded to bfloat16.
+    const size_t tok_row0 = (size_t)b * T + (size_t)kt * kTile;
+    auto store_proj = [&](const ProjectionOut& pr, int kk, int d4, const f32x4& v) {
+        const size_t at = (tok_row0 + kk) * (size_t)pr.width + kHeadDim * kv + d4;
+        *(f32x4*)(pr.f32 + at) = v;
+        *(uint2*)(pr.b16 + at) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+    };
+    const bool proj = kproj.f32 != nullptr;
     to_lds(dkacc0, dkacc1);
     __syncthreads();
     for (int idx = tid; idx < 64 * 16; idx += kThreads) {  // dK[key][d]: 16 float4s per key
@@ -450,18 +473,20 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
 #pragma unroll
         for (int g = 1; g < GW; ++g) v += *(const f32x4*)&red[(g * 64 + kk) * kRedRow + d4];
         v *= s;
-        *(f32x4*)(dK + (key_row0 + kk) * kHeadDim + d4) = v;
+        if (proj) store_proj(kproj, kk, d4, v);
+        else *(f32x4*)(dK + (key_row0 + kk) * kHeadDim + d4) = v;
     }
     __syncthreads();
     to_lds(dvacc0, dvacc1);
     __syncthreads();
-    if (v_rows) {
+    if (v_rows || proj) {
         for (int idx = tid; idx < 64 * 16; idx += kThreads) {  // dV[key][d]: 16 float4s per key
             const int kk = idx >> 4, d4 = (idx & 15) * 4;
             f32x4 v = *(const f32x4*)&red[kk * kRedRow + d4];
 #pragma unroll
             for (int g = 1; g < GW; ++g) v += *(const f32x4*)&red[(g * 64 + kk) * kRedRow + d4];
-            *(f32x4*)(dVt + (key_row0 + kk) * kHeadDim + d4) = v;
+            if (proj) store_proj(vproj, kk, d4, v);
+            else *(f32x4*)(dVt + (key_row0 + kk) * kHeadDim + d4) = v;
         }
         return;
     }
@@ -516,17 +541,6 @@ constexpr int kDqVmPerStep = 2 + 4;               // per lane: K DMA, dS loads
 constexpr int kDqKWait = 4 + (kDqLead - 1) * kDqVmPerStep;
 static_assert(kDqKWait == 22, "the s_waitcnt immediate below");
 
-// Round to nearest even bfloat16: the upper half of the binary32 word after
-// adding half an ulp of the kept part, ties going to the even one (inputs are
-// finite).
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-    const uint32_t u = __float_as_uint(x);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
-    return make_uint2(bf16_bits(a) | (bf16_bits(b) << 16), bf16_bits(c) | (bf16_bits(d) << 16));
-}
-
 // ROT: the epilogue of the query pass's rotated variant (StreamingAttentionSM86
 // page, "dQ = s (the sum), turned back by the inverse half-split rotation"):
 // the scaled pair (x1, x2) of columns c and c + 32 at position p becomes
@@ -534,14 +548,19 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d)
 // each product rounded as the page's FMUL then FFMA, and is stored as
 // bfloat16 at columns 64 h + c and 64 h + c + 32 of row p of the token-major
 // [B][T][width] projection gradient; dQ itself is not written.
-template <bool CAUSAL, bool VARLEN, bool ROT>
+// PROJ: the projection variant's epilogue (same page, "dQ = s (the sum)
+// stored straight into a fused projection's gradient"): the scaled dQ row
+// goes to columns 64 h + c of row p of a token-major gradient, once in
+// binary32 and once rounded to bfloat16, instead of the [B][H][T][64] plane.
+enum { kDqPlain = 0, kDqRotated = 1, kDqProjection = 2 };
+template <bool CAUSAL, bool VARLEN, int MODE>
 __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __restrict__ K,
                                                                const half_t* __restrict__ dS,
                                                                float* __restrict__ dQ,
                                                                const int32_t* __restrict__ seqlens, float s,
                                                                int T, int H, int KV, int n_qblk, int BH,
                                                                int block_order, long long tiles_per_head,
-                                                               DqRotation rot) {
+                                                               DqEpilogue rot) {
     __shared__ __attribute__((aligned(16))) half_t lds[kDqDepth][kKTileHalves];  // K tiles
     __shared__ __attribute__((aligned(16))) half_t dsl[kDqWaves][kDsBlockHalves];  // each wave's dS block
 
@@ -720,7 +739,25 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
         }
         if (!wave_rows) return;
         const float scale = (!VARLEN || q < len) ? s : 0.0f;
-        if (ROT) {
+        if (MODE == kDqProjection) {
+            const size_t row = ((size_t)b * T + q) * (size_t)rot.width + kHeadDim * h;
+            float* o32 = rot.out32 + row;
+            uint16_t* o16 = rot.out + row;
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int c0 = 8 * rg + 4 * hi;
+                f32x4 v0 = {acc0[4 * rg], acc0[4 * rg + 1], acc0[4 * rg + 2], acc0[4 * rg + 3]};
+                f32x4 v1 = {acc1[4 * rg], acc1[4 * rg + 1], acc1[4 * rg + 2], acc1[4 * rg + 3]};
+                v0 *= scale;
+                v1 *= scale;
+                *(f32x4*)(o32 + c0) = v0;
+                *(f32x4*)(o32 + 32 + c0) = v1;
+                *(uint2*)(o16 + c0) = pack_bf16x4(v0[0], v0[1], v0[2], v0[3]);
+                *(uint2*)(o16 + 32 + c0) = pack_bf16x4(v1[0], v1[1], v1[2], v1[3]);
+            }
+            return;
+        }
+        if (MODE == kDqRotated) {
             // Each lane holds columns c = 8 rg + 4 hi + 0..3 and c + 32 of its query's row.
             const float* cr = rot.cos + (size_t)q * 32;
             const float* sr = rot.sin + (size_t)q * 32;
@@ -767,10 +804,10 @@ template <bool CAUSAL, bool VARLEN>
 void launch_key_gw(int GW, dim3 grid, hipStream_t stream, const half_t* Q, const half_t* K, const half_t* Vt,
                    const half_t* dO, const float* L, const float* D, half_t* dS, float* dK, float* dVt,
                    const int32_t* seqlens, float c, float s, int T, int H, int KV, int nkt, int BKV, int order,
-                   long long tph, int v_rows) {
+                   long long tph, int v_rows, const ProjectionOut& kproj, const ProjectionOut& vproj) {
 #define SA_KEY_LAUNCH(gw)                                                                                    \
     hipLaunchKernelGGL((sa_key_kernel<CAUSAL, VARLEN, gw>), grid, dim3(128 * gw), 0, stream, Q, K, Vt, dO, L, \
-                       D, dS, dK, dVt, seqlens, c, s, T, H, KV, nkt, BKV, order, tph, v_rows)
+                       D, dS, dK, dVt, seqlens, c, s, T, H, KV, nkt, BKV, order, tph, v_rows, kproj, vproj)
     switch (GW) {
         case 4: SA_KEY_LAUNCH(4); break;
         case 3: SA_KEY_LAUNCH(3); break;
@@ -812,9 +849,9 @@ hipError_t launch_row_terms(const Shape& sh, const void* dO, const void* O, floa
     return hipGetLastError();
 }
 
-hipError_t launch_key_pass(const Shape& sh, const void* Q, const void* K, const void* Vt, const void* dO,
-                           const float* L, const float* D, void* dS, float c, float s, float* dK, float* dVt,
-                           hipStream_t stream) {
+hipError_t launch_key_pass_to(const Shape& sh, const void* Q, const void* K, const void* Vt, const void* dO,
+                              const float* L, const float* D, void* dS, float c, float s, float* dK, float* dVt,
+                              const ProjectionOut& kproj, const ProjectionOut& vproj, hipStream_t stream) {
     const int nkt = sh.T / kTile, BKV = sh.batch * sh.kv_heads;
     const int GW = key_gw(sh.heads / sh.kv_heads);
     dim3 grid((unsigned)key_pass_blocks(sh));
@@ -823,7 +860,7 @@ hipError_t launch_key_pass(const Shape& sh, const void* Q, const void* K, const 
         constexpr bool C = decltype(causal_tag)::value, V = decltype(varlen_tag)::value;
         launch_key_gw<C, V>(GW, grid, stream, (const half_t*)Q, (const half_t*)K, (const half_t*)Vt,
                             (const half_t*)dO, L, D, (half_t*)dS, dK, dVt, sh.seqlens, c, s, sh.T, sh.heads,
-                            sh.kv_heads, nkt, BKV, sh.block_order, tph, sh.v_rows);
+                            sh.kv_heads, nkt, BKV, sh.block_order, tph, sh.v_rows, kproj, vproj);
     };
     using T_ = std::true_type;
     using F_ = std::false_type;
@@ -835,8 +872,21 @@ hipError_t launch_key_pass(const Shape& sh, const void* Q, const void* K, const 
     return hipGetLastError();
 }
 
-template <bool ROT>
-hipError_t launch_dq(const Shape& sh, const void* K, const void* dS, float s, float* dQ, const DqRotation& rot,
+hipError_t launch_key_pass(const Shape& sh, const void* Q, const void* K, const void* Vt, const void* dO,
+                           const float* L, const float* D, void* dS, float c, float s, float* dK, float* dVt,
+                           hipStream_t stream) {
+    const ProjectionOut none{nullptr, nullptr, 0};
+    return launch_key_pass_to(sh, Q, K, Vt, dO, L, D, dS, c, s, dK, dVt, none, none, stream);
+}
+
+hipError_t launch_key_pass_projection(const Shape& sh, const void* Q, const void* K, const void* Vt,
+                                      const void* dO, const float* L, const float* D, void* dS, float c, float s,
+                                      const ProjectionOut& kproj, const ProjectionOut& vproj, hipStream_t stream) {
+    return launch_key_pass_to(sh, Q, K, Vt, dO, L, D, dS, c, s, nullptr, nullptr, kproj, vproj, stream);
+}
+
+template <int MODE>
+hipError_t launch_dq(const Shape& sh, const void* K, const void* dS, float s, float* dQ, const DqEpilogue& rot,
                      hipStream_t stream) {
     const int n_qblk = (sh.T + kDqRows - 1) / kDqRows, BH = sh.batch * sh.heads;
     dim3 grid((unsigned)dq_pass_blocks(sh)), block(kDqThreads);
@@ -846,21 +896,28 @@ hipError_t launch_dq(const Shape& sh, const void* K, const void* dS, float s, fl
                            sh.T, sh.heads, sh.kv_heads, n_qblk, BH, sh.block_order, tph, rot);
     };
     if (sh.causal) {
-        if (sh.seqlens) go(sa_dq_kernel<true, true, ROT>); else go(sa_dq_kernel<true, false, ROT>);
+        if (sh.seqlens) go(sa_dq_kernel<true, true, MODE>); else go(sa_dq_kernel<true, false, MODE>);
     } else {
-        if (sh.seqlens) go(sa_dq_kernel<false, true, ROT>); else go(sa_dq_kernel<false, false, ROT>);
+        if (sh.seqlens) go(sa_dq_kernel<false, true, MODE>); else go(sa_dq_kernel<false, false, MODE>);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_dq_pass(const Shape& sh, const void* K, const void* dS, float s, float* dQ,
                           hipStream_t stream) {
-    return launch_dq<false>(sh, K, dS, s, dQ, DqRotation{nullptr, nullptr, nullptr, 0}, stream);
+    return launch_dq<kDqPlain>(sh, K, dS, s, dQ, DqEpilogue{nullptr, nullptr, nullptr, nullptr, 0}, stream);
 }
 
 hipError_t launch_dq_pass_rotated(const Shape& sh, const void* K, const void* dS, float s, const float* cos_t,
                                   const float* sin_t, void* dqkv, int width, hipStream_t stream) {
-    return launch_dq<true>(sh, K, dS, s, nullptr, DqRotation{cos_t, sin_t, (uint16_t*)dqkv, width}, stream);
+    return launch_dq<kDqRotated>(sh, K, dS, s, nullptr,
+                                 DqEpilogue{cos_t, sin_t, (uint16_t*)dqkv, nullptr, width}, stream);
+}
+
+hipError_t launch_dq_pass_projection(const Shape& sh, const void* K, const void* dS, float s, const ProjectionOut& q,
+                                     hipStream_t stream) {
+    return launch_dq<kDqProjection>(sh, K, dS, s, nullptr,
+                                    DqEpilogue{nullptr, nullptr, (uint16_t*)q.b16, q.f32, q.width}, stream);
 }
 
 }  // namespace sa

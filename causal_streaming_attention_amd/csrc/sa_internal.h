@@ -34,14 +34,27 @@ hipError_t launch_dq_pass(const Shape& sh, const void* K, const void* dS, float 
 // The dQ pass with the rotated epilogue: dQ turned back by the inverse
 // half-split rotation (tables cos_t, sin_t fp32 [T][32]) and stored as the
 // bfloat16 Q slice of the token-major projection gradient dqkv [B][T][width].
-struct DqRotation {
+struct DqEpilogue {
     const float* cos;
     const float* sin;
-    uint16_t* out;
+    uint16_t* out;    // bfloat16 output (rotated slice, or the projection's bfloat16 copy)
+    float* out32;     // the projection's binary32 copy
     int width;
 };
 hipError_t launch_dq_pass_rotated(const Shape& sh, const void* K, const void* dS, float s, const float* cos_t,
                                   const float* sin_t, void* dqkv, int width, hipStream_t stream);
+// One column slice of a fused projection's token-major gradient [B][T][width]:
+// head u's 64 values of row p at f32 / b16 + (b T + p) width + 64 u + d.
+struct ProjectionOut {
+    float* f32;
+    uint16_t* b16;
+    int width;
+};
+hipError_t launch_key_pass_projection(const Shape& sh, const void* Q, const void* K, const void* Vt,
+                                      const void* dO, const float* L, const float* D, void* dS, float c, float s,
+                                      const ProjectionOut& kproj, const ProjectionOut& vproj, hipStream_t stream);
+hipError_t launch_dq_pass_projection(const Shape& sh, const void* K, const void* dS, float s, const ProjectionOut& q,
+                                     hipStream_t stream);
 // The two-launch backward's query pass (D and dQ); its key launch is
 // launch_key_pass with dS == nullptr (no score gradients stored).
 hipError_t launch_query_pass(const Shape& sh, const void* dO, const void* O, const float* L, const void* Q,

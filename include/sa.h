@@ -203,6 +203,30 @@ sa_status sa_dq_pass_rotated(const sa_shape* shape, const void* K, const void* d
                              const float* cos_t, const float* sin_t, void* dqkv, int width, void* stream);
 
 /*
+ * The split backward storing its gradients straight into a fused QKV
+ * projection's gradient (StreamingAttentionSM86 page: the query launch's
+ * "dQ = s (the sum) stored straight into a fused projection's gradient" and
+ * the key launch's "dK = s (the sum) and dV stored straight into a fused
+ * projection's gradient"): row terms, key pass and dQ pass as sa_backward_ex,
+ * but dQ, dK and dV are written token-major, each in binary32 and rounded to
+ * bfloat16 (nearest even), instead of into the [head] planes.
+ *   dQ32, dQ16:  the Q slice: row p (of batch b) at (b T + p) width, query
+ *                head h's 64 values at columns 64 h .. 64 h + 63 of it;
+ *   dK32, dK16:  the K slice, K/V head kv at columns 64 kv + 0..63 (the
+ *                group sum, scaled by s);
+ *   dV32, dV16:  the V slice, the same columns, unscaled.
+ * Each pointer names its slice's first column (the caller offsets it into
+ * the shared [B][T][width] buffers); fp32 pointers and bf16 pointers are
+ * 16-byte aligned.  width: row length in elements, a multiple of 8 and at
+ * least 64 heads; the slices must fit in the rows.  Other columns are left
+ * untouched; padded rows and keys get zeros.  D and dS as sa_backward_ex.
+ */
+sa_status sa_backward_projection(const sa_shape* shape, const void* dO, const void* O, const float* L, float* D,
+                                 void* dS, size_t dS_bytes, const void* Q, const void* K, const void* Vt,
+                                 float c, float s, float* dQ32, void* dQ16, float* dK32, void* dK16,
+                                 float* dV32, void* dV16, int width, void* stream);
+
+/*
  * The backward in two launches, with no dS workspace (StreamingAttentionSM86
  * page, banner "The backward pass, deterministic and in two launches (no
  * atomics)"): the query launch forms D and dQ, recomputing S, P and dP per

@@ -213,3 +213,25 @@ def test_rotated_dq_pass_rejects_bad_arguments(lib):
     assert call(ptrs, sc=float("inf")) == sa.SA_ERR_ARGUMENT
     assert call(ptrs, width=W - 8) == sa.SA_ERR_ARGUMENT      # narrower than the Q slice
     assert call(ptrs, width=W + 4) == sa.SA_ERR_ARGUMENT      # not a multiple of 8
+
+
+def test_projection_backward_rejects_bad_arguments(lib):
+    s = shape()
+    need = sa.sa_backward_workspace_bytes(s)
+    W = 64 * (s.heads + 2 * s.kv_heads)
+
+    def call(p, ws=need, c=0.18, sc=0.125, width=W):
+        return lib.sa_backward_projection(ctypes.byref(s), p[0], p[1], p[2], p[3], p[4], ws, p[5], p[6], p[7], c,
+                                          sc, p[8], p[9], p[10], p[11], p[12], p[13], width, None)
+
+    ptrs = [FAKE] * 14   # dO O L D dS Q K Vt dQ32 dQ16 dK32 dK16 dV32 dV16
+    for i in range(14):
+        bad = list(ptrs)
+        bad[i] = None
+        assert call(bad) == sa.SA_ERR_NULL
+        bad[i] = FAKE + 8
+        assert call(bad) == sa.SA_ERR_ALIGN
+    assert call(ptrs, ws=need - 1) == sa.SA_ERR_WORKSPACE
+    assert call(ptrs, c=-1.0) == sa.SA_ERR_ARGUMENT
+    assert call(ptrs, width=64 * s.heads - 8) == sa.SA_ERR_ARGUMENT
+    assert call(ptrs, width=W + 2) == sa.SA_ERR_ARGUMENT

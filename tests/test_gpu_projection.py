@@ -1,0 +1,80 @@
+"""GPU parity of the backward that stores dQ, dK and dV straight into a fused
+QKV projection's token-major gradient (sa_backward_projection): the binary32
+slices equal the split path's dQ, dK, dV bitwise (same arithmetic), the
+bfloat16 copies are their round-to-nearest-even values bit for bit, the slices
+match the oracle's layout of its own gradients, columns outside the slices are
+untouched, and padded rows are zero."""
+import numpy as np
+import pytest
+import torch
+
+import causal_streaming_attention_amd as sa
+import oracle
+from causal_streaming_attention_amd.workloads import SCALE, WORKLOADS, generate, make_inputs
+from parity_util import C, check_grad, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+SENT32 = -7.25
+SENT16 = 0x3FC0      # bfloat16 1.5
+EXTRA = 16           # columns past the three slices, never written
+
+
+def _rne_bf16(x32):
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _projection(buf, H, KV):
+    B, T = buf.B, buf.T
+    width = 64 * (H + 2 * KV) + EXTRA
+    g32 = torch.full((B, T, width), SENT32, dtype=torch.float32, device="cuda")
+    g16 = torch.full((B, T, width), SENT16, dtype=torch.int16, device="cuda")
+    qc, kc, vc = 0, 64 * H, 64 * (H + KV)
+    p32, p16 = g32.data_ptr(), g16.data_ptr()
+    sa.sa_backward_projection(buf.shape, buf.dO, buf.O, buf.L, buf.D, buf.dS, buf.ws_bytes, buf.Q, buf.K, buf.Vt,
+                              C, SCALE, p32 + 4 * qc, p16 + 2 * qc, p32 + 4 * kc, p16 + 2 * kc, p32 + 4 * vc,
+                              p16 + 2 * vc, width)
+    torch.cuda.synchronize()
+    return g32.cpu().numpy(), g16.cpu().numpy().view(np.uint16), width, (qc, kc, vc)
+
+
+CASES = [
+    # name, B, T, H, KV, causal, seqlens
+    ("mha_t128_causal", 1, 128, 2, 2, True, None),
+    ("gqa2_t320_causal", 2, 320, 4, 2, True, None),
+    ("varlen_gqa2_full_b3_t256", 3, 256, 4, 2, False, [256, 77, 0]),
+    ("varlen_causal_b2_t192", 2, 192, 2, 1, True, [130, 191]),
+]
+
+
+def _check(x, causal, H, KV, name, with_oracle=True):
+    buf, got = run_gpu(x, causal)                       # the split path: dQ, dK, dVt planes
+    g32, g16, width, (qc, kc, vc) = _projection(buf, H, KV)
+    # the same values, laid out, bitwise
+    want32 = oracle.projection_slices(got["dQ"], got["dK"], got["dVt"], width, qc, kc, vc).astype(np.float32)
+    used = slice(0, vc + 64 * KV)
+    assert np.array_equal(g32[:, :, used], want32[:, :, used]), f"{name}: binary32 slices differ from the planes"
+    assert np.array_equal(g16[:, :, used], _rne_bf16(g32[:, :, used])), f"{name}: bfloat16 copies not RNE"
+    assert np.all(g32[:, :, vc + 64 * KV:] == SENT32) and np.all(g16[:, :, vc + 64 * KV:] == SENT16), \
+        f"{name}: columns past the slices were written"
+    if x["seqlens"] is not None:
+        for b, n in enumerate(x["seqlens"]):
+            assert np.all(g32[b, n:, used] == 0.0), f"{name}: padded rows not zero"
+    if with_oracle:
+        ref = oracle.backward(x["Q"], x["K"], x["Vt"], x["dO"], s=SCALE, causal=causal, seqlens=x["seqlens"])
+        want = oracle.projection_slices(ref["dQ"], ref["dK"], ref["dVt"], width, qc, kc, vc)
+        for nm, sl in (("dQ", slice(qc, kc)), ("dK", slice(kc, vc)), ("dV", slice(vc, vc + 64 * KV))):
+            check_grad(nm, g32[:, :, sl].astype(np.float64), want[:, :, sl], name)
+
+
+@pytest.mark.parametrize("name,B,T,H,KV,causal,seqlens", CASES, ids=[c[0] for c in CASES])
+def test_projection_small(name, B, T, H, KV, causal, seqlens):
+    say(f"case projection {name}")
+    _check(make_inputs(B, T, H, KV, seed=400 + T + H, seqlens=seqlens), causal, H, KV, name)
+
+
+def test_projection_causal_gqa_t4096_workload():
+    w = WORKLOADS["causal_gqa_t4096"]
+    say(f"case projection {w.name}")
+    _check(generate(w), w.causal, w.heads, w.kv_heads, w.name, with_oracle=False)
