@@ -463,6 +463,34 @@ def main():
                       "note": "sa_dq_pass_rotated alone, back to back: dQ turned back by the inverse half-split "
                               "rotation and stored as the bfloat16 Q slice of a token-major [T][width] gradient"}
 
+    # The backward storing dQ, dK, dV straight into a fused QKV projection's
+    # token-major gradient (binary32 and bfloat16), timed like the headline's
+    # backward on the same inputs.
+    projection = None
+    if not args.headline_only:
+        pw = (w.heads + 2 * w.kv_heads) * HEAD_DIM
+        g32 = torch.zeros(w.batch, w.T, pw, dtype=torch.float32, device="cuda")
+        g16 = torch.zeros(w.batch, w.T, pw, dtype=torch.int16, device="cuda")
+        qc, kc, vc = 0, HEAD_DIM * w.heads, HEAD_DIM * (w.heads + w.kv_heads)
+        p32, p16 = g32.data_ptr(), g16.data_ptr()
+
+        def step_proj(ev=None):
+            if ev: ev[0].record(stream)
+            sa.sa_forward_ex(sh, buf.Q, buf.K, buf.Vt, buf.O, buf.L, c, stream)
+            if ev: ev[1].record(stream)
+            sa.sa_backward_projection(sh, buf.dO, buf.O, buf.L, buf.D, buf.dS, buf.ws_bytes, buf.Q, buf.K, buf.Vt,
+                                      c, SCALE, p32 + 4 * qc, p16 + 2 * qc, p32 + 4 * kc, p16 + 2 * kc,
+                                      p32 + 4 * vc, p16 + 2 * vc, pw, stream)
+            if ev: ev[2].record(stream)
+
+        for _ in range(args.warmup):
+            step_proj()
+        proj_ms, proj_per, _ = timed(step_proj, 2)
+        projection = {"ms_per_step": round(proj_ms, 4), "tflops": round(fl["total"] / (proj_ms * 1e-3) / 1e12, 2),
+                      "backward_ms": round(proj_per[1], 4), "projection_width": pw,
+                      "note": "the headline step with sa_backward_projection: dQ, dK, dV written token-major into "
+                              "a fused QKV projection's gradient, binary32 and bfloat16"}
+
     if args.calibrate_copy_mb > 0:
         n = args.calibrate_copy_mb << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -493,6 +521,8 @@ def main():
         out["v_rows"] = v_rows
     if dq_rotated is not None:
         out["dq_pass_rotated"] = dq_rotated
+    if projection is not None:
+        out["projection_backward"] = projection
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x)
     print(json.dumps(out), flush=True)
