@@ -78,3 +78,16 @@ def test_projection_causal_gqa_t4096_workload():
     w = WORKLOADS["causal_gqa_t4096"]
     say(f"case projection {w.name}")
     _check(generate(w), w.causal, w.heads, w.kv_heads, w.name, with_oracle=False)
+
+
+def test_projection_v_rows_matches_v_transposed():
+    """With V passed as rows, the key pass loads V's rows directly; the slices are bitwise the V^T path's."""
+    say("case projection v_rows")
+    B, T, H, KV = 2, 256, 4, 2
+    x = make_inputs(B, T, H, KV, seed=451, seqlens=[256, 130])
+    outs = []
+    for v_rows in (False, True):
+        buf, _ = run_gpu(x, True, v_rows=v_rows)
+        g32, g16, _, _ = _projection(buf, H, KV)
+        outs.append((g32, g16))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
