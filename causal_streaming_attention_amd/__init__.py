@@ -57,6 +57,8 @@ _SIGS = {
     "sa_dq_pass_rotated": (_I, [_SP, _V, _V, _Z, _F, _V, _V, _V, _I, _V]),
     "sa_backward_projection": (_I, [_SP, _V, _V, _V, _V, _V, _Z, _V, _V, _V, _F, _F, _V, _V, _V, _V, _V, _V, _I,
                                     _V]),
+    "sa_backward_two_pass_projection": (_I, [_SP, _V, _V, _V, _V, _V, _V, _V, _F, _F, _V, _V, _V, _V, _V, _V, _I,
+                                             _V]),
     "sa_query_pass": (_I, [_SP, _V, _V, _V, _V, _V, _V, _F, _F, _V, _V, _V]),
     "sa_backward_two_pass": (_I, [_SP, _V, _V, _V, _V, _V, _V, _V, _F, _F, _V, _V, _V, _V]),
     "sa_status_string": (ctypes.c_char_p, [_I]),
@@ -182,6 +184,15 @@ def sa_backward_projection(shape, dO, O, L, D, dS, dS_bytes, Q, K, Vt, c, s, dQ3
                                            dS_bytes, _ptr(Q), _ptr(K), _ptr(Vt), c, s, _ptr(dQ32), _ptr(dQ16),
                                            _ptr(dK32), _ptr(dK16), _ptr(dV32), _ptr(dV16), width, _stream(stream)),
            "sa_backward_projection")
+
+
+def sa_backward_two_pass_projection(shape, dO, O, L, D, Q, K, Vt, c, s, dQ32, dQ16, dK32, dK16, dV32, dV16, width,
+                                    stream=None):
+    _check(native().sa_backward_two_pass_projection(ctypes.byref(shape), _ptr(dO), _ptr(O), _ptr(L), _ptr(D),
+                                                    _ptr(Q), _ptr(K), _ptr(Vt), c, s, _ptr(dQ32), _ptr(dQ16),
+                                                    _ptr(dK32), _ptr(dK16), _ptr(dV32), _ptr(dV16), width,
+                                                    _stream(stream)),
+           "sa_backward_two_pass_projection")
 
 
 def sa_query_pass(shape, dO, O, L, Q, K, Vt, c, s, D, dQ, stream=None):

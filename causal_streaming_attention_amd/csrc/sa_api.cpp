@@ -202,6 +202,24 @@ sa_status sa_backward_two_pass(const sa_shape* shape, const void* dO, const void
     return from_hip(sa::launch_key_pass(sh, Q, K, Vt, dO, L, D, nullptr, c, s, dK, dVt, strm));
 }
 
+sa_status sa_backward_two_pass_projection(const sa_shape* shape, const void* dO, const void* O, const float* L,
+                                          float* D, const void* Q, const void* K, const void* Vt, float c, float s,
+                                          float* dQ32, void* dQ16, float* dK32, void* dK16, float* dV32, void* dV16,
+                                          int width, void* stream) {
+    sa_status st = sa_check_shape(shape);
+    if (st != SA_OK) return st;
+    if ((st = check_ptrs({dO, O, L, D, Q, K, Vt, dQ32, dQ16, dK32, dK16, dV32, dV16})) != SA_OK) return st;
+    if (!scale_ok(c) || !scale_ok(s)) return SA_ERR_ARGUMENT;
+    if (width % 8 != 0 || (long long)width < 64ll * shape->heads) return SA_ERR_ARGUMENT;
+    const sa::Shape sh = to_shape(shape);
+    hipStream_t strm = (hipStream_t)stream;
+    const sa::ProjectionOut q{dQ32, (uint16_t*)dQ16, width}, k{dK32, (uint16_t*)dK16, width},
+        v{dV32, (uint16_t*)dV16, width};
+    if ((st = from_hip(sa::launch_query_pass_projection(sh, dO, O, L, Q, K, Vt, c, s, D, q, strm))) != SA_OK)
+        return st;
+    return from_hip(sa::launch_key_pass_projection(sh, Q, K, Vt, dO, L, D, nullptr, c, s, k, v, strm));
+}
+
 const char* sa_status_string(int status) {
     switch (status) {
         case SA_OK: return "ok";

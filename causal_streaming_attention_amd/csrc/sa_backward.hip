@@ -24,16 +24,6 @@ namespace sa {
 
 namespace {
 
-// Round to nearest even bfloat16: the upper half of the binary32 word after
-// adding half an ulp of the kept part, ties going to the even one (inputs are
-// finite).
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-    const uint32_t u = __float_as_uint(x);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
-    return make_uint2(bf16_bits(a) | (bf16_bits(b) << 16), bf16_bits(c) | (bf16_bits(d) << 16));
-}
 
 
 // ---------------------------------------------------------------------------

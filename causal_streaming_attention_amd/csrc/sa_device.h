@@ -90,6 +90,17 @@ __device__ __forceinline__ void pair_schedule(int block, int n_groups, int group
 // record count in bytes.
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
+// Round to nearest even bfloat16: the upper half of the binary32 word after
+// adding half an ulp of the kept part, ties going to the even one (inputs are
+// finite).
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
+    return make_uint2(bf16_bits(a) | (bf16_bits(b) << 16), bf16_bits(c) | (bf16_bits(d) << 16));
+}
+
 // Round to nearest even binary16.
 __device__ __forceinline__ half_t to_half(float x) { return (half_t)x; }
 

@@ -55,6 +55,9 @@ hipError_t launch_key_pass_projection(const Shape& sh, const void* Q, const void
                                       const ProjectionOut& kproj, const ProjectionOut& vproj, hipStream_t stream);
 hipError_t launch_dq_pass_projection(const Shape& sh, const void* K, const void* dS, float s, const ProjectionOut& q,
                                      hipStream_t stream);
+hipError_t launch_query_pass_projection(const Shape& sh, const void* dO, const void* O, const float* L,
+                                        const void* Q, const void* K, const void* Vt, float c, float s, float* D,
+                                        const ProjectionOut& qproj, hipStream_t stream);
 // The two-launch backward's query pass (D and dQ); its key launch is
 // launch_key_pass with dS == nullptr (no score gradients stored).
 hipError_t launch_query_pass(const Shape& sh, const void* dO, const void* O, const float* L, const void* Q,

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kQpThreads, 2) void sa_query_kernel(
     const half_t* __restrict__ Q, const half_t* __restrict__ K, const half_t* __restrict__ Vt,
     const half_t* __restrict__ dO, const half_t* __restrict__ O, const float* __restrict__ L,
     float* __restrict__ D, float* __restrict__ dQ, const int32_t* __restrict__ seqlens, float c, float s,
-    int T, int H, int KV, int n_qtiles, int BH, int block_order) {
+    int T, int H, int KV, int n_qtiles, int BH, int block_order, ProjectionOut qproj) {
     // K tile j lives in buffer j % 3: its dQ products are issued one tile late,
     // beside the next tile's vector work, while tile j + 1 is staged.
     __shared__ __attribute__((aligned(16))) half_t kls[3][kQpTile];  // K tiles [key][d]
@@ -321,8 +321,27 @@ __global__ __launch_bounds__(kQpThreads, 2) void sa_query_kernel(
 
         if (!wave_rows) return;
         // dQ = s dQ^T: lane holds d = 8 (r / 4) + 4 hi + r % 4 of query q.
-        float* dq = dQ + row_id * kHeadDim;
         const float scale = (!VARLEN || q < len) ? s : 0.0f;
+        if (qproj.f32) {
+            // Projection variant (same page, the shared query pass stored
+            // straight into a fused projection's gradient): row q of the
+            // token-major gradient, columns 64 h + d, binary32 and bfloat16.
+            const size_t at = ((size_t)b * T + q) * (size_t)qproj.width + kHeadDim * h;
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int c0 = 8 * rg + 4 * hi;
+                f32x4 v0 = {dq0[4 * rg], dq0[4 * rg + 1], dq0[4 * rg + 2], dq0[4 * rg + 3]};
+                f32x4 v1 = {dq1[4 * rg], dq1[4 * rg + 1], dq1[4 * rg + 2], dq1[4 * rg + 3]};
+                v0 *= scale;
+                v1 *= scale;
+                *(f32x4*)(qproj.f32 + at + c0) = v0;
+                *(f32x4*)(qproj.f32 + at + 32 + c0) = v1;
+                *(uint2*)(qproj.b16 + at + c0) = pack_bf16x4(v0[0], v0[1], v0[2], v0[3]);
+                *(uint2*)(qproj.b16 + at + 32 + c0) = pack_bf16x4(v1[0], v1[1], v1[2], v1[3]);
+            }
+            return;
+        }
+        float* dq = dQ + row_id * kHeadDim;
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
             f32x4 v0 = {dq0[4 * rg], dq0[4 * rg + 1], dq0[4 * rg + 2], dq0[4 * rg + 3]};
@@ -345,16 +364,16 @@ size_t query_pass_blocks(const Shape& sh) {
     return (sh.block_order == 0 ? (n_qtiles + 1) / 2 : n_qtiles) * sh.batch * sh.heads;
 }
 
-hipError_t launch_query_pass(const Shape& sh, const void* dO, const void* O, const float* L, const void* Q,
-                             const void* K, const void* Vt, float c, float s, float* D, float* dQ,
-                             hipStream_t stream) {
+hipError_t launch_query_pass_to(const Shape& sh, const void* dO, const void* O, const float* L, const void* Q,
+                                const void* K, const void* Vt, float c, float s, float* D, float* dQ,
+                                const ProjectionOut& qproj, hipStream_t stream) {
     const int n_qtiles = (sh.T + kQpRows - 1) / kQpRows;
     const int BH = sh.batch * sh.heads;
     dim3 grid((unsigned)query_pass_blocks(sh)), block(kQpThreads);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, stream, (const half_t*)Q, (const half_t*)K, (const half_t*)Vt,
                            (const half_t*)dO, (const half_t*)O, L, D, dQ, sh.seqlens, c, s, sh.T, sh.heads,
-                           sh.kv_heads, n_qtiles, BH, sh.block_order);
+                           sh.kv_heads, n_qtiles, BH, sh.block_order, qproj);
     };
     const bool varlen = sh.seqlens != nullptr;
     auto pick = [&](auto rows_tag) {
@@ -370,6 +389,18 @@ hipError_t launch_query_pass(const Shape& sh, const void* dO, const void* O, con
     if (sh.v_rows) pick(std::true_type{});
     else pick(std::false_type{});
     return hipGetLastError();
+}
+
+hipError_t launch_query_pass(const Shape& sh, const void* dO, const void* O, const float* L, const void* Q,
+                             const void* K, const void* Vt, float c, float s, float* D, float* dQ,
+                             hipStream_t stream) {
+    return launch_query_pass_to(sh, dO, O, L, Q, K, Vt, c, s, D, dQ, ProjectionOut{nullptr, nullptr, 0}, stream);
+}
+
+hipError_t launch_query_pass_projection(const Shape& sh, const void* dO, const void* O, const float* L,
+                                        const void* Q, const void* K, const void* Vt, float c, float s, float* D,
+                                        const ProjectionOut& qproj, hipStream_t stream) {
+    return launch_query_pass_to(sh, dO, O, L, Q, K, Vt, c, s, D, nullptr, qproj, stream);
 }
 
 }  // namespace sa

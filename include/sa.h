@@ -254,6 +254,19 @@ sa_status sa_backward_two_pass(const sa_shape* shape, const void* dO, const void
                                float* D, const void* Q, const void* K, const void* Vt, float c, float s,
                                float* dQ, float* dK, float* dVt, void* stream);
 
+/*
+ * The two-launch backward storing into a fused QKV projection's gradient
+ * (same page: the shared query pass's and the key launch's projection
+ * epilogues): sa_query_pass writing D and dQ's slice, then the key pass
+ * without a dS store writing dK's and dV's slices.  The slices, their
+ * layout, width and alignment are as sa_backward_projection's; D as
+ * sa_backward_two_pass.
+ */
+sa_status sa_backward_two_pass_projection(const sa_shape* shape, const void* dO, const void* O, const float* L,
+                                          float* D, const void* Q, const void* K, const void* Vt, float c, float s,
+                                          float* dQ32, void* dQ16, float* dK32, void* dK16, float* dV32, void* dV16,
+                                          int width, void* stream);
+
 /* Static text for a status value ("unknown status" for anything else). */
 const char* sa_status_string(int status);
 

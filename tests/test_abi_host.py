@@ -235,3 +235,22 @@ def test_projection_backward_rejects_bad_arguments(lib):
     assert call(ptrs, c=-1.0) == sa.SA_ERR_ARGUMENT
     assert call(ptrs, width=64 * s.heads - 8) == sa.SA_ERR_ARGUMENT
     assert call(ptrs, width=W + 2) == sa.SA_ERR_ARGUMENT
+
+
+def test_two_pass_projection_backward_rejects_bad_arguments(lib):
+    s = shape()
+    W = 64 * (s.heads + 2 * s.kv_heads)
+
+    def call(p, c=0.18, sc=0.125, width=W):
+        return lib.sa_backward_two_pass_projection(ctypes.byref(s), p[0], p[1], p[2], p[3], p[4], p[5], p[6], c, sc,
+                                                   p[7], p[8], p[9], p[10], p[11], p[12], width, None)
+
+    ptrs = [FAKE] * 13   # dO O L D Q K Vt dQ32 dQ16 dK32 dK16 dV32 dV16
+    for i in range(13):
+        bad = list(ptrs)
+        bad[i] = None
+        assert call(bad) == sa.SA_ERR_NULL
+        bad[i] = FAKE + 8
+        assert call(bad) == sa.SA_ERR_ALIGN
+    assert call(ptrs, sc=float("nan")) == sa.SA_ERR_ARGUMENT
+    assert call(ptrs, width=W - 4) == sa.SA_ERR_ARGUMENT

@@ -25,16 +25,20 @@ def _rne_bf16(x32):
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
-def _projection(buf, H, KV):
+def _projection(buf, H, KV, two_pass=False):
     B, T = buf.B, buf.T
     width = 64 * (H + 2 * KV) + EXTRA
     g32 = torch.full((B, T, width), SENT32, dtype=torch.float32, device="cuda")
     g16 = torch.full((B, T, width), SENT16, dtype=torch.int16, device="cuda")
     qc, kc, vc = 0, 64 * H, 64 * (H + KV)
     p32, p16 = g32.data_ptr(), g16.data_ptr()
-    sa.sa_backward_projection(buf.shape, buf.dO, buf.O, buf.L, buf.D, buf.dS, buf.ws_bytes, buf.Q, buf.K, buf.Vt,
-                              C, SCALE, p32 + 4 * qc, p16 + 2 * qc, p32 + 4 * kc, p16 + 2 * kc, p32 + 4 * vc,
-                              p16 + 2 * vc, width)
+    slices = (p32 + 4 * qc, p16 + 2 * qc, p32 + 4 * kc, p16 + 2 * kc, p32 + 4 * vc, p16 + 2 * vc)
+    if two_pass:
+        sa.sa_backward_two_pass_projection(buf.shape, buf.dO, buf.O, buf.L, buf.D, buf.Q, buf.K, buf.Vt, C, SCALE,
+                                           *slices, width)
+    else:
+        sa.sa_backward_projection(buf.shape, buf.dO, buf.O, buf.L, buf.D, buf.dS, buf.ws_bytes, buf.Q, buf.K,
+                                  buf.Vt, C, SCALE, *slices, width)
     torch.cuda.synchronize()
     return g32.cpu().numpy(), g16.cpu().numpy().view(np.uint16), width, (qc, kc, vc)
 
@@ -91,3 +95,21 @@ def test_projection_v_rows_matches_v_transposed():
         g32, g16, _, _ = _projection(buf, H, KV)
         outs.append((g32, g16))
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("name,B,T,H,KV,causal,seqlens", CASES, ids=[c[0] for c in CASES])
+def test_two_pass_projection_small(name, B, T, H, KV, causal, seqlens):
+    """The two-launch backward's projection variant: bitwise the two-launch planes, RNE copies, untouched
+    columns, zero padding."""
+    say(f"case two-pass projection {name}")
+    x = make_inputs(B, T, H, KV, seed=500 + T + H, seqlens=seqlens)
+    buf, got = run_gpu(x, causal, path="two_pass")
+    g32, g16, width, (qc, kc, vc) = _projection(buf, H, KV, two_pass=True)
+    want32 = oracle.projection_slices(got["dQ"], got["dK"], got["dVt"], width, qc, kc, vc).astype(np.float32)
+    used = slice(0, vc + 64 * KV)
+    assert np.array_equal(g32[:, :, used], want32[:, :, used]), f"{name}: binary32 slices differ from the planes"
+    assert np.array_equal(g16[:, :, used], _rne_bf16(g32[:, :, used])), f"{name}: bfloat16 copies not RNE"
+    assert np.all(g32[:, :, vc + 64 * KV:] == SENT32) and np.all(g16[:, :, vc + 64 * KV:] == SENT16)
+    if seqlens is not None:
+        for b, n in enumerate(seqlens):
+            assert np.all(g32[b, n:, used] == 0.0), f"{name}: padded rows not zero"
