@@ -491,6 +491,22 @@ def main():
                       "note": "the headline step with sa_backward_projection: dQ, dK, dV written token-major into "
                               "a fused QKV projection's gradient, binary32 and bfloat16"}
 
+        def step_proj2(ev=None):
+            if ev: ev[0].record(stream)
+            sa.sa_forward_ex(sh, buf.Q, buf.K, buf.Vt, buf.O, buf.L, c, stream)
+            if ev: ev[1].record(stream)
+            sa.sa_backward_two_pass_projection(sh, buf.dO, buf.O, buf.L, buf.D, buf.Q, buf.K, buf.Vt, c, SCALE,
+                                               p32 + 4 * qc, p16 + 2 * qc, p32 + 4 * kc, p16 + 2 * kc,
+                                               p32 + 4 * vc, p16 + 2 * vc, pw, stream)
+            if ev: ev[2].record(stream)
+
+        for _ in range(args.warmup):
+            step_proj2()
+        p2_ms, p2_per, _ = timed(step_proj2, 2)
+        projection["two_pass"] = {"ms_per_step": round(p2_ms, 4),
+                                  "tflops": round(fl["total"] / (p2_ms * 1e-3) / 1e12, 2),
+                                  "backward_ms": round(p2_per[1], 4)}
+
     if args.calibrate_copy_mb > 0:
         n = args.calibrate_copy_mb << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
