@@ -214,6 +214,35 @@ def summarize_profile(dirs, workload, command):
     print("\n".join(lines))
 
 
+def summarize_all_kernels(d, workload, command):
+    """Write profiles/kernel_trace_all_paths_<workload>.txt: every kernel instantiation of a full bench run
+    (the headline and the variants timed beside it), by name with its template arguments."""
+    import re
+    stats = [r for r in _read_csv(_find(d, "kernel_stats.csv")) if "sa_" in r["Name"]]
+    lines = [f"# rocprofv3 kernel trace of the full bench (every path), workload {workload}", f"# command: {command}",
+             "# template arguments: forward / query <causal, varlen, V as rows>; key <causal, varlen, waves pairs "
+             "per group>; dq <causal, varlen, epilogue: 0 plain, 1 rotated, 2 projection>; the key pass's dS store, "
+             "V rows and projection stores are run-time choices within one instantiation", "",
+             f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}  kernel"]
+    def readable(mangled):
+        # sa::<anon>::<name><literal template arguments>: a length-prefixed name, then L<b|i><value>E items
+        m = re.match(r"_ZN2sa12_GLOBAL__N_1(\d+)", mangled)
+        if not m:
+            return mangled
+        n = int(m.group(1))
+        name = mangled[m.end():m.end() + n]
+        args = re.findall(r"L([bi])(\d+)E", mangled[m.end() + n:].split("EEv")[0] + "E")
+        vals = [("true" if v == "1" else "false") if t == "b" else v for t, v in args]
+        return f"{name}<{', '.join(vals)}>"
+
+    for r, name in sorted(((r, readable(r["Name"])) for r in stats), key=lambda t: t[1]):
+        lines.append(f"{int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} {float(r['MinNs']) / 1e3:>10.2f} "
+                     f"{float(r['MaxNs']) / 1e3:>10.2f}  {name}")
+    with open(os.path.join(ROOT, "profiles", f"kernel_trace_all_paths_{workload}.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 SQ_COUNTERS = ["SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
                "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"]
 
@@ -270,6 +299,9 @@ def main():
                          "passes of a --calibrate-copy-mb run) into profiles/ and exit")
     ap.add_argument("--summarize-counters", metavar="DIR",
                     help="summarize one rocprofv3 --pmc run of the SQ counters into profiles/ and exit")
+    ap.add_argument("--summarize-all-kernels", metavar="DIR",
+                    help="summarize a rocprofv3 --kernel-trace --stats run of the full bench (every path) into "
+                         "profiles/ and exit")
     ap.add_argument("--profile-command", default="", help="command line recorded in the summaries")
     args = ap.parse_args()
     if args.summarize_profile:
@@ -277,6 +309,9 @@ def main():
         return
     if args.summarize_counters:
         summarize_counters(args.summarize_counters, args.workload, args.profile_command)
+        return
+    if args.summarize_all_kernels:
+        summarize_all_kernels(args.summarize_all_kernels, args.workload, args.profile_command)
         return
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
