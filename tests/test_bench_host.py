@@ -28,3 +28,23 @@ def test_flop_convention_of_the_bench_workload():
     assert fl["dq_pass"] == 2 * 64 * pairs
     assert abs(fl["forward"] / 1e9 - 68.72) < 0.01
     assert abs(fl["total"] / 1e9 - 240.52) < 0.01
+
+
+def test_all_kernels_summary_names_instantiations(tmp_path, monkeypatch):
+    """The all-paths summary turns mangled instantiation names into name<arguments> and keeps only the
+    library's kernels."""
+    import bench
+    d = tmp_path / "prof"
+    d.mkdir()
+    (d / "run_kernel_stats.csv").write_text(
+        "Name,Calls,TotalDurationNs,AverageNs,Percentage,MinNs,MaxNs,StdDev\n"
+        '"_ZN2sa12_GLOBAL__N_112sa_dq_kernelILb1ELb0ELi2EEEvPKDF16_S3_PfPKifiiiiiixNS_10DqEpilogueE",'
+        "4,400000,100000,50,99000,101000,1\n"
+        '"_ZN2sa12_GLOBAL__N_113sa_key_kernelILb0ELb1ELi4EEEvPKDF16_",2,380000,190000,40,189000,191000,1\n'
+        '"at::native::vectorized_elementwise_kernel<4>",1,1000,1000,1,1000,1000,0\n')
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    bench.summarize_all_kernels(str(d), "w", "cmd")
+    text = (tmp_path / "profiles" / "kernel_trace_all_paths_w.txt").read_text()
+    assert "sa_dq_kernel<true, false, 2>" in text and "sa_key_kernel<false, true, 4>" in text
+    assert "at::native" not in text
