@@ -330,3 +330,17 @@ def test_projection_slices_give_the_fused_projection_input_gradient():
     want = Xt.grad.numpy()
     got = Gm @ W.T
     assert np.max(np.abs(got - want)) <= 1e-9 * max(1.0, np.max(np.abs(want)))
+
+
+def test_oracle_matches_torch_with_boosted_keys():
+    """The long-context workload's score distribution (Q, K with variance 2, a few key rows scaled by 8):
+    base-2 logits of order 100, where a softmax without its running maximum would overflow."""
+    x = make_inputs(1, 128, 4, 2, seed=77, qk_std=math.sqrt(2.0), boost_frac=0.05, boost=8.0)
+    r = oracle.backward(x["Q"], x["K"], x["Vt"], x["dO"], s=SCALE, causal=True)
+    ref = torch_reference(x["Q"], x["K"], x["Vt"], x["dO"], True, None)
+    assert np.max(np.abs(ref["L"])) > 30.0          # the regime the workload stresses
+    np.testing.assert_allclose(r["O"], ref["O"], rtol=0, atol=1e-11)
+    np.testing.assert_allclose(r["L"], ref["L"], rtol=0, atol=1e-10)
+    for k in ("dQ", "dK", "dVt"):
+        scale = max(1.0, float(np.max(np.abs(ref[k]))))
+        np.testing.assert_allclose(r[k], ref[k], rtol=0, atol=1e-10 * scale, err_msg=k)
