@@ -113,3 +113,23 @@ def test_two_pass_projection_small(name, B, T, H, KV, causal, seqlens):
     if seqlens is not None:
         for b, n in enumerate(seqlens):
             assert np.all(g32[b, n:, used] == 0.0), f"{name}: padded rows not zero"
+
+
+def test_projection_and_rotated_outputs_equal_across_block_orders():
+    """Block order 1 (one tile per block, plain order) gives the same bits as the paired, XCD-grouped order."""
+    say("case projection block orders")
+    B, T, H, KV = 1, 512, 8, 2
+    x = make_inputs(B, T, H, KV, seed=470)
+    theta = np.random.default_rng(471).uniform(-np.pi, np.pi, size=(T, 32))
+    cos_t = torch.from_numpy(np.cos(theta).astype(np.float32)).cuda()
+    sin_t = torch.from_numpy(np.sin(theta).astype(np.float32)).cuda()
+    outs = []
+    for order in (0, 1):
+        buf, _ = run_gpu(x, True, block_order=order)
+        g32, g16, width, _ = _projection(buf, H, KV)
+        rot = torch.zeros((B, T, width), dtype=torch.int16, device="cuda")
+        sa.sa_dq_pass_rotated(buf.shape, buf.K, buf.dS, buf.ws_bytes, SCALE, cos_t, sin_t, rot, width)
+        torch.cuda.synchronize()
+        outs.append((g32, g16, rot.cpu().numpy()))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
