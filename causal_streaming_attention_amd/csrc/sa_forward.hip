@@ -26,11 +26,12 @@
 // The loop is software-pipelined: while tile j's softmax runs on the vector
 // unit, the wave's matrix-core work is tile j + 1's scores and tile j - 1's
 // P V, issued between the softmax instructions, at raised wave priority so
-// that of the two waves on a SIMD the one with matrix work issues first.  The
-// maximum used for the
-// exponents moves only when some row of the wave exceeds it by more than 8
-// (base 2), so P <= 2^8 and the O/l rescale is rare; O / l and L = m + log2 l
-// are the same quantities whichever maximum the exponents used.  Blocks take
+// that of the two waves on a SIMD the one with matrix work issues first.  P
+// is first formed with the exponents' current maximum; the maximum is taken
+// and moved (and P formed again) only on the wave's first tile and when some
+// lane's sum of P exceeds 2^8, so P <= 2^8, the row maximum costs nothing on
+// the other tiles and the O/l rescale is rare; O / l and L = m + log2 l are
+// the same quantities whichever maximum the exponents used.  Blocks take
 // the query tiles (n - 1 - p, p) in pairs of equal causal length, with the
 // heads that share a kv head kept on one XCD (pair_schedule).
 #include "sa_device.h"
@@ -61,9 +62,9 @@ __device__ __forceinline__ int vr_key(int r) { return (((r >> 1) & 1) << 2) | ((
 __device__ __forceinline__ int vr_off(int r, int col) {
     return r * kHeadDim + (((col >> 3) ^ vr_key(r)) << 3) + (col & 7);
 }
-// The running maximum used for the exponents moves only when some row of the
-// wave sees a scaled score more than this far (base 2) above it, so P <= 2^8.
-constexpr float kMaxSlack = 8.0f;
+// The running maximum used for the exponents moves only when some lane's sum
+// of its 32 P in a tile exceeds this bound (P >= 0, so then every P <= 2^8).
+constexpr float kMaxSum = 256.0f;
 
 // Zero the halves of an 8-half chunk at positions >= keep (keep may be <= 0 or >= 8).
 __device__ __forceinline__ uint4 clear_tail(uint4 v, int keep) {
@@ -152,7 +153,8 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
     }
 
     f32x16 oacc0 = zero16(), oacc1 = zero16();  // O^T, d blocks 0..31 and 32..63
-    float m = kNegInf, lsum = 0.0f;
+    // m: the exponents' maximum; neg_m = -m, or 0 while m = -inf.
+    float m = kNegInf, neg_m = 0.0f, lsum = 0.0f;
     // O's move to a new maximum is applied one step late, just before the
     // next tile's products are added: the step that raises the maximum still
     // has the previous tile's products in flight.
@@ -266,6 +268,21 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
         }
     };
 
+    auto exponentials = [&](const f32x16& s0, const f32x16& s1, float nm, uint32_t (&p)[16]) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            const float p0 = exp2_fast(__builtin_fmaf(s0[r], c, nm));
+            const float p1 = exp2_fast(__builtin_fmaf(s0[r + 1], c, nm));
+            const float p2 = exp2_fast(__builtin_fmaf(s1[r], c, nm));
+            const float p3 = exp2_fast(__builtin_fmaf(s1[r + 1], c, nm));
+            sum += (p0 + p1) + (p2 + p3);
+            p[r >> 1] = pack_half2(p0, p1);
+            p[8 + (r >> 1)] = pack_half2(p2, p3);
+        }
+        return sum;
+    };
+
     // One key tile j.  cur holds tile j's scores; the step forms tile j + 1's
     // scores into nxt and adds tile j - 1's products (P in pprev) to O while
     // it turns cur into P (pcur), then restages and synchronises.
@@ -305,39 +322,37 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
             scores(kls[(j + 1) & 1], nxt0, nxt1);
             pv(vls[j == 0 ? 0 : (j + 2) % 3], pprev);
 
-            // Row maximum of the raw scores (c > 0, so max(S) c = max(S c)).
-            float mx = fmaxf(cur0[0], cur1[0]);
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, cur0[r]), cur1[r]);
-            const float mxc = max_halves(mx) * c;
-            // The exponents' maximum moves (for every row of the wave) only
-            // when some row exceeds it by more than the slack; a row with no
-            // admitted key so far has m = -inf and always counts as exceeding.
-            const bool grow = __builtin_amdgcn_ballot_w64(mxc > m + kMaxSlack) != 0;
-            const float m_new = grow ? fmaxf(m, mxc) : m;
-            const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-            const float neg_m = -m_use;
-            // P = 2^(S c - m), the row's partial sum, and P^T packed as the B
-            // operand of the four 16-key k-steps.
-            float psum = 0.0f;
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float p0 = exp2_fast(__builtin_fmaf(cur0[r], c, neg_m));
-                const float p1 = exp2_fast(__builtin_fmaf(cur0[r + 1], c, neg_m));
-                const float p2 = exp2_fast(__builtin_fmaf(cur1[r], c, neg_m));
-                const float p3 = exp2_fast(__builtin_fmaf(cur1[r + 1], c, neg_m));
-                psum += (p0 + p1) + (p2 + p3);
-                pcur[r >> 1] = pack_half2(p0, p1);
-                pcur[8 + (r >> 1)] = pack_half2(p2, p3);
-            }
-            // l moves to the new maximum now, O (which still lacks tile
-            // j - 1's products) at the start of the next step.
-            alpha = grow ? exp2_fast(m - m_use) : 1.0f;
-            rescale = grow;
-            lsum = __builtin_fmaf(lsum, alpha, psum);
-            m = m_new;
+            // P = 2^(S c - m) with the exponents' current maximum, the lane's
+            // partial sum, and P^T packed as the B operand of the four 16-key
+            // k-steps.
+            float psum = exponentials(cur0, cur1, neg_m, pcur);
             SA_FWD_INTERLEAVE();
             __builtin_amdgcn_s_setprio(0);
+            // The maximum moves (for every row of the wave, each to its own
+            // running maximum) on the wave's first tile, which sets it, and
+            // when some P may exceed 2^8; P is then formed again.  After the
+            // first tile a row still at m = -inf has no admitted key at all
+            // (key 0 is admitted to every query below the length), so its P
+            // stay 0.
+            if (j == 0 || __builtin_amdgcn_ballot_w64(psum > kMaxSum) != 0) {
+                // Row maximum of the raw scores (c > 0, so max(S) c = max(S c)).
+                float mx = fmaxf(cur0[0], cur1[0]);
+#pragma unroll
+                for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, cur0[r]), cur1[r]);
+                const float m_new = fmaxf(m, max_halves(mx) * c);
+                const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
+                psum = exponentials(cur0, cur1, -m_use, pcur);
+                // l moves to the new maximum now, O (which still lacks tile
+                // j - 1's products) at the start of the next step.
+                alpha = exp2_fast(m - m_use);
+                rescale = true;
+                lsum = __builtin_fmaf(lsum, alpha, psum);
+                m = m_new;
+                neg_m = -m_use;
+            } else {
+                rescale = false;
+                lsum += psum;
+            }
         }
 
         // K_{j+2} replaces K_j (last read in the previous step) and V_{j+1}
