@@ -161,15 +161,39 @@ def summarize_profile(dirs, workload, command):
     and profiles/hbm_traffic_<workload>.txt.  Counter bytes are scaled by what the same counter
     reads for the closing device copy, whose bytes are known."""
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    import re
     trace_dir = dirs[0]
     stats = _read_csv(_find(trace_dir, "kernel_stats.csv"))
-    lines = [f"# rocprofv3 kernel trace, workload {workload}", f"# command: {command}", "",
-             f"{'kernel':<12} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}"]
+    # The bench's per-kernel figures average the last K launches (its second timed pass); the
+    # stats' average also holds the warm-up launches, which start on a low clock.
+    m = re.search(r"bench\.py --steps (\d+)", command)
+    last_k = int(m.group(1)) if m else 0
+    per_dispatch = {}
+    if last_k:
+        try:
+            rows = _read_csv(_find(trace_dir, "kernel_trace.csv"))
+        except FileNotFoundError:
+            rows = []
+        for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
+            for short, key in KERNEL_NAMES.items():
+                if key in r["Kernel_Name"]:
+                    per_dispatch.setdefault(short, []).append(
+                        (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = [f"# rocprofv3 kernel trace, workload {workload}", f"# command: {command}"]
+    if per_dispatch:
+        lines.append(f"# last{last_k}_us: average over each kernel's last {last_k} launches (the timed steps the "
+                     "bench's per-kernel figures average); avg_us includes the warm-up launches")
+    lines += ["", f"{'kernel':<12} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}"
+              + (f" {'last' + str(last_k) + '_us':>10}" if per_dispatch else "")]
     for short, key in KERNEL_NAMES.items():
         for r in stats:
             if key in r["Name"]:
-                lines.append(f"{short:<12} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
-                             f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f}")
+                line = (f"{short:<12} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
+                        f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f}")
+                if per_dispatch.get(short):
+                    tail = per_dispatch[short][-last_k:]
+                    line += f" {sum(tail) / len(tail):>10.2f}"
+                lines.append(line)
     with open(os.path.join(ROOT, "profiles", f"kernel_trace_{workload}.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -185,7 +209,6 @@ def summarize_profile(dirs, workload, command):
             vals = [float(r["Counter_Value"]) for r in rows if key in r["Kernel_Name"]]
             if vals:
                 per[label]["kernels"][short] = sum(vals) / len(vals)
-    import re
     m = re.search(r"--calibrate-copy-mb[= ](\d+)", command)
     copy_bytes = int(m.group(1)) << 20 if m else None
     if copy_bytes is None:

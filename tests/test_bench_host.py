@@ -48,3 +48,28 @@ def test_all_kernels_summary_names_instantiations(tmp_path, monkeypatch):
     text = (tmp_path / "profiles" / "kernel_trace_all_paths_w.txt").read_text()
     assert "sa_dq_kernel<true, false, 2>" in text and "sa_key_kernel<false, true, 4>" in text
     assert "at::native" not in text
+
+
+def test_trace_summary_averages_the_timed_launches(tmp_path, monkeypatch):
+    """The kernel-trace summary adds each kernel's average over its last K launches (K from the recorded
+    bench command), the launches the bench's own per-kernel figures cover, beside the all-launch average."""
+    import bench
+    d = tmp_path / "prof"
+    d.mkdir()
+    name = "_ZN2sa12_GLOBAL__N_117sa_forward_kernelILb1ELb0ELb0EEEv"
+    durs = [300.0, 200.0, 100.0, 110.0]  # microseconds: two warm-up launches, then two timed ones
+    (d / "run_kernel_stats.csv").write_text(
+        "Name,Calls,TotalDurationNs,AverageNs,Percentage,MinNs,MaxNs,StdDev\n"
+        f'"{name}",4,710000,177500,100,100000,300000,1\n')
+    rows = ["Kind,Dispatch_Id,Kernel_Name,Start_Timestamp,End_Timestamp"]
+    t = 1000
+    for i, us in enumerate(durs):
+        rows.append(f'KERNEL_DISPATCH,{i + 1},"{name}",{t},{t + int(us * 1000)}')
+        t += 10 ** 7
+    (d / "run_kernel_trace.csv").write_text("\n".join(rows) + "\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    bench.summarize_profile([str(d)], "w", "rocprofv3 --kernel-trace -- python3 bench.py --steps 2 --headline-only")
+    text = (tmp_path / "profiles" / "kernel_trace_w.txt").read_text()
+    line = [l for l in text.splitlines() if l.startswith("forward")][0].split()
+    assert float(line[2]) == 177.5 and float(line[5]) == 105.0
