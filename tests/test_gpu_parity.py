@@ -61,6 +61,42 @@ def test_small_full_parity(name, B, T, H, KV, causal, seqlens):
     _check_all(x, causal, name)
 
 
+def _structured_scores(T, H, tile_offsets, seed, slope=0.0, noise=0.1):
+    """Q rows along one +-1 direction u, K row j = g_j u, both plus Gaussian noise, so that the base-2
+    score of key j is close to the same g_j c |u|^2 for every query: tile k's keys sit tile_offsets[k]
+    above tile 0's, and `slope` adds a rise per key.  The noise keeps the softmax from collapsing onto
+    one key, where dP - D cancels and the fp16 O inside D (the pages' reading) alone would cost dQ
+    about 1% relative L2; with these settings that share stays under 0.4% in binary64 estimates."""
+    rng = np.random.default_rng(seed)
+    c = SCALE / np.log(2.0)
+    u = rng.choice([-1.0, 1.0], size=64)
+    g = np.array([0.5 + (tile_offsets[j // 64] + slope * j) / (c * 64.0) for j in range(T)])
+    Q = (u[None, None, :] + noise * rng.standard_normal((1, H, T, 64))).astype(np.float16)
+    K = (g[None, None, :, None] * u[None, None, None, :]
+         + noise * rng.standard_normal((1, 1, T, 64))).astype(np.float16)
+    V = rng.standard_normal((1, 1, T, 64)).astype(np.float16)
+    dO = rng.standard_normal((1, H, T, 64)).astype(np.float16)
+    return {"Q": Q, "K": K, "Vt": np.ascontiguousarray(V.transpose(0, 1, 3, 2)), "dO": dO, "seqlens": None}
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_scores_rising_tile_after_tile(causal):
+    """Base-2 scores rising by about 6 per 64-key tile: under the old maximum a lane's 32 P of a new tile
+    sum past 2^8 on most tiles, so the exponents' maximum moves and O and l are rescaled tile after tile."""
+    say(f"case rising_scores causal={causal}")
+    x = _structured_scores(512, 2, [0.0] * 8, seed=901, slope=6.0 / 64.0, noise=0.3)
+    _check_all(x, causal, f"rising_scores_{causal}")
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_scores_stepping_up_by_less_than_eight(causal):
+    """Whole tiles 4, then 2 more, then 3.5 more above the first: no single P exceeds 2^8 under the old
+    maximum, but 32 keys of 2^4 (or 2^3.5) sum past 2^8 in a lane and move it, while 32 of 2^2 do not."""
+    say(f"case stepped_scores causal={causal}")
+    x = _structured_scores(256, 2, [0.0, 4.0, 6.0, 9.5], seed=902)
+    _check_all(x, causal, f"stepped_scores_{causal}")
+
+
 def test_tiny_causal_t128_workload():
     w = WORKLOADS["tiny_causal_t128"]
     say(f"case {w.name}")
