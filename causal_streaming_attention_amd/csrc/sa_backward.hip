@@ -353,6 +353,14 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
             }
             if ((lane & 31) >= keep) (lane < 32 ? Ls : Ds)[lane & 31] = 0.0f;
         }
+        // This item's score and dP operands first, so that one wait covers
+        // them and the previous item's transposed operands.
+        half8 qa[4], da[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            qa[q4] = *(const half8*)(Qs + swz(l32, 16 * q4 + 8 * hi));
+            da[q4] = *(const half8*)(dOs + swz(l32, 16 * q4 + 8 * hi));
+        }
         // The previous item's transposed operands; once they are in registers
         // its buffer takes the next item.
         half4 t[16];
@@ -364,9 +372,9 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
         // dS exact zeros.
         f32x16 sacc = zero16(), pacc = zero16();
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) sacc = mfma32(*(const half8*)(Qs + swz(l32, 16 * q4 + 8 * hi)), kf[q4], sacc);
+        for (int q4 = 0; q4 < 4; ++q4) sacc = mfma32(qa[q4], kf[q4], sacc);
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) pacc = mfma32(*(const half8*)(dOs + swz(l32, 16 * q4 + 8 * hi)), vf[q4], pacc);
+        for (int q4 = 0; q4 < 4; ++q4) pacc = mfma32(da[q4], vf[q4], pacc);
         f32x4 lv[4], dv[4];
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
