@@ -268,6 +268,9 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
         }
     };
 
+    // P = 2^(S c + nm) for a tile's 32 scores of this lane's query (nm is
+    // minus the exponents' maximum), packed as binary16 pairs in accumulator
+    // order; returns the lane's binary32 sum of the unrounded P.
     auto exponentials = [&](const f32x16& s0, const f32x16& s1, float nm, uint32_t (&p)[16]) {
         float sum = 0.0f;
 #pragma unroll
