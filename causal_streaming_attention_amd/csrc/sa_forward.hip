@@ -336,8 +336,11 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
             // when some P may exceed 2^8; P is then formed again.  After the
             // first tile a row still at m = -inf has no admitted key at all
             // (key 0 is admitted to every query below the length), so its P
-            // stay 0.
-            if (j == 0 || __builtin_amdgcn_ballot_w64(psum > kMaxSum) != 0) {
+            // stay 0.  (The first-tile test sits inside the ballot: as a
+            // separate || it lets the compiler sink the exponentials above
+            // below the branch on steps where j may be 0, out of the
+            // interleaved stretch.)
+            if (__builtin_amdgcn_ballot_w64((psum > kMaxSum) | (j == 0)) != 0) {
                 // Row maximum of the raw scores (c > 0, so max(S) c = max(S c)).
                 float mx = fmaxf(cur0[0], cur1[0]);
 #pragma unroll
