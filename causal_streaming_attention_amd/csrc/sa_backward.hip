@@ -371,6 +371,10 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
         // half, padding) goes through the same code: the mask makes its P and
         // dS exact zeros.
         f32x16 sacc = zero16(), pacc = zero16();
+        // Raised wave priority from here to the end of the vector work: of
+        // the two waves on a SIMD, the one with matrix work in hand issues
+        // first.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) sacc = mfma32(qa[q4], kf[q4], sacc);
 #pragma unroll
@@ -382,11 +386,8 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
             dv[rg] = *(const f32x4*)(Ds + 8 * rg + 4 * hi);
         }
         // The previous item's products go into the matrix pipe behind these,
-        // one between every few of this item's vector instructions.  The
-        // wave runs that stretch at raised priority, so that of the two waves
-        // on a SIMD the one with matrix work in hand issues first.
+        // one between every few of this item's vector instructions.
         __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_setprio(1);
         accumulate(t, wp, wd);
         float p[16], g[16];
 #pragma unroll
