@@ -371,9 +371,9 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
         // half, padding) goes through the same code: the mask makes its P and
         // dS exact zeros.
         f32x16 sacc = zero16(), pacc = zero16();
-        // Raised wave priority from here to the end of the vector work: of
-        // the two waves on a SIMD, the one with matrix work in hand issues
-        // first.
+        // Raised wave priority from here to the end of the item: of the two
+        // waves on a SIMD, the one past its operand reads and waits (with
+        // matrix and vector work in hand) issues first.
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) sacc = mfma32(qa[q4], kf[q4], sacc);
@@ -396,7 +396,6 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
             g[r] = p[r] * (pacc[r] - dv[r >> 2][r & 3]);
         }
         SA_KEY_INTERLEAVE();
-        __builtin_amdgcn_s_setprio(0);
         const bool need_mask = (CAUSAL && qb < kbase + 31) || (VARLEN && (qb + kSubRows > len || kbase + 32 > len));
         if (need_mask) {
 #pragma unroll
@@ -428,6 +427,7 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
             __builtin_nontemporal_store(half8_from_words(wd[0], wd[1], wd[2], wd[3]), (half8*)dsp);
             __builtin_nontemporal_store(half8_from_words(wd[4], wd[5], wd[6], wd[7]), (half8*)(dsp + 512));
         }
+        __builtin_amdgcn_s_setprio(0);  // the next item's reads and waits at normal priority
         head = next_head;
         sub = next_sub;
     }
