@@ -9,7 +9,7 @@ import oracle
 from causal_streaming_attention_amd.workloads import SCALE, WORKLOADS, generate, make_inputs
 from parity_util import (check_forward, check_grad, full_reference, rel_l2, run_gpu, sample_cols, sample_rows,
                          say)
-from test_gpu_parity import SMALL, _gradient_sums
+from test_gpu_parity import SMALL, _gradient_sums, _structured_scores
 
 pytestmark = pytest.mark.gpu
 PATH = "two_pass"
@@ -34,6 +34,16 @@ def test_two_pass_small_full_parity(name, B, T, H, KV, causal, seqlens):
     say(f"case two-pass {name}")
     x = make_inputs(B, T, H, KV, seed=100 + T + H, seqlens=seqlens)
     _check_all(x, causal, name)
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_two_pass_structured_scores(causal):
+    """The split path's rising and stepped score recipes (the forward's exponent maximum moves tile after
+    tile, or on lane sums of P): the query pass recomputes P from the forward's L on these rows too."""
+    for name, x in (("rising", _structured_scores(512, 2, [0.0] * 8, seed=901, slope=6.0 / 64.0, noise=0.3)),
+                    ("stepped", _structured_scores(256, 2, [0.0, 4.0, 6.0, 9.5], seed=902))):
+        say(f"case {name}_scores two-pass causal={causal}")
+        _check_all(x, causal, f"{name}_scores_{causal}")
 
 
 def test_two_pass_causal_mha_t1024_workload():
