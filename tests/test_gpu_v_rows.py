@@ -44,6 +44,19 @@ def test_v_rows_small(name, B, T, H, KV, causal, seqlens):
         check_grad(k, rows[k], ref[k], name)
 
 
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_v_rows_structured_scores_bitwise(causal):
+    """The rising and stepped score recipes (the forward's exponent maximum moves tile after tile, or on
+    lane sums of P): the V-rows instantiation takes the same growth steps, bit for bit."""
+    from test_gpu_parity import _structured_scores
+    for name, x in (("rising", _structured_scores(512, 2, [0.0] * 8, seed=901, slope=6.0 / 64.0, noise=0.3)),
+                    ("stepped", _structured_scores(256, 2, [0.0, 4.0, 6.0, 9.5], seed=902))):
+        say(f"case v_rows {name}_scores causal={causal}")
+        _, rows = run_gpu(x, causal, v_rows=True)
+        _, cols = run_gpu(x, causal)
+        _same(rows, cols, f"{name}_scores_{causal}")
+
+
 def test_v_rows_causal_gqa_t4096_bitwise():
     """The benchmark's shape and launch configuration (its V^T path is parity-tested
     against the oracle in the workload tests)."""
