@@ -668,11 +668,16 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
 
         auto step = [&](const int kt, half8 (&cur)[4], half8 (&ahead)[4]) {
             issue(kt + kDqLead, ahead);
-            if (kt >= kt_end) return;  // padding step of the unrolled loop: loads only
+            // dS tile kt, issued four steps back: 24 loads are younger.  The
+            // wait ties the slot and sits on every path, also where the tile
+            // is not used (a padding step of the unrolled loop, or a tile past
+            // this wave's rows): the compiler must not reuse or copy the
+            // slot's registers (say, for the next step's addresses) while its
+            // loads may still land in them.
+            static_assert((kDqLead) * kDqVmPerStep == 24, "the s_waitcnt immediate below");
+            asm volatile("s_waitcnt vmcnt(24)" : "+v"(cur[0]), "+v"(cur[1]), "+v"(cur[2]), "+v"(cur[3]));
+            if (kt >= kt_end) return;  // padding step: loads only
             if (kt < kt_end_w) {
-                // dS tile kt, issued four steps back: 24 loads are younger.
-                static_assert((kDqLead) * kDqVmPerStep == 24, "the s_waitcnt immediate below");
-                asm volatile("s_waitcnt vmcnt(24)" : "+v"(cur[0]), "+v"(cur[1]), "+v"(cur[2]), "+v"(cur[3]));
                 // The block goes through this wave's LDS copy (each 1 KB run
                 // padded by 64 bytes between its two 512-byte halves) and comes
                 // back transposed: lane (query l32, hi) gets the 8 keys of
@@ -736,6 +741,17 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
             step(kt + 3, sl3, sl2);
             step(kt + 4, sl4, sl3);
         }
+        // The padding steps (and, with no tile to walk, the prologue) leave
+        // dS loads in flight into slots nobody reads: the compiler, which does
+        // not see them, would reuse those registers in the epilogue while a
+        // late load could still land in them.  Drain them here, tying every
+        // slot so that no register of theirs is reused before the wait.
+        asm volatile("s_waitcnt vmcnt(0)"
+                     : "+v"(sl0[0]), "+v"(sl0[1]), "+v"(sl0[2]), "+v"(sl0[3]), "+v"(sl1[0]), "+v"(sl1[1]),
+                       "+v"(sl1[2]), "+v"(sl1[3]), "+v"(sl2[0]), "+v"(sl2[1]) :: "memory");
+        asm volatile("s_waitcnt vmcnt(0)"
+                     : "+v"(sl2[2]), "+v"(sl2[3]), "+v"(sl3[0]), "+v"(sl3[1]), "+v"(sl3[2]), "+v"(sl3[3]),
+                       "+v"(sl4[0]), "+v"(sl4[1]), "+v"(sl4[2]), "+v"(sl4[3]) :: "memory");
         if (!wave_rows) return;
         const float scale = (!VARLEN || q < len) ? s : 0.0f;
         if (MODE == kDqProjection) {
