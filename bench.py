@@ -302,6 +302,83 @@ def summarize_counters(d, workload, command):
     print("\n".join(lines))
 
 
+def clock_settle(seconds: float):
+    """Keep the GPU busy with plain fp16 matrix products for about `seconds` before the warm-up.
+
+    An idle MI355X sits at a low shader clock and ramps up over tens of milliseconds of load, so a short
+    warm-up leaves the timed steps on a rising clock (a cold step then runs faster than the headline).
+    This load is not the attention step and is not timed."""
+    import torch
+    a = torch.randn(4096, 4096, dtype=torch.float16, device="cuda")
+    b = torch.randn(4096, 4096, dtype=torch.float16, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            a = torch.matmul(a, b) * 1e-3
+        torch.cuda.synchronize()
+        n += 8
+    return {"seconds": round(time.perf_counter() - t0, 3), "fp16_gemms_4096": n,
+            "note": "GPU held busy before the warm-up so the timed steps start at the loaded clock; not timed"}
+
+
+def time_workload(name: str, steps: int, warmup: int, block_order: int = 0):
+    """One workload's fwd+bwd step (the headline's four launches), timed like the headline: `warmup` steps,
+    then `steps` steps between one pair of events, then the same with events between the launches."""
+    import torch
+    import causal_streaming_attention_amd as sa
+    from causal_streaming_attention_amd.workloads import SCALE, WORKLOADS, generate
+    w = WORKLOADS[name]
+    x = generate(w)
+    buf = sa.Buffers(x, w.causal, block_order=block_order)
+    c = sa.base2_scale(SCALE)
+    sh = buf.shape
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        sa.sa_forward_ex(sh, buf.Q, buf.K, buf.Vt, buf.O, buf.L, c, stream)
+        if ev: ev[1].record(stream)
+        sa.sa_row_terms(sh, buf.dO, buf.O, buf.D, stream)
+        if ev: ev[2].record(stream)
+        sa.sa_key_pass(sh, buf.Q, buf.K, buf.Vt, buf.dO, buf.L, buf.D, buf.dS, buf.ws_bytes, c, SCALE, buf.dK,
+                       buf.dVt, stream)
+        if ev: ev[3].record(stream)
+        sa.sa_dq_pass(sh, buf.K, buf.dS, buf.ws_bytes, SCALE, buf.dQ, stream)
+        if ev: ev[4].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record(stream)
+    for _ in range(steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = max(a.elapsed_time(b) / steps, (time.perf_counter() - t0) * 1e3 / steps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for k in range(steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    names = ["forward", "row_terms", "key_pass", "dq_pass"]
+    per = {n: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)]))
+           for i, n in enumerate(names)}
+    fl = kernel_flops(w, x["seqlens"])
+    tf = fl["total"] / (ms * 1e-3) / 1e12
+    out = {"ms_per_step": round(ms, 4), "tflops": round(tf, 2), "pct_mfma_peak": round(100 * tf / PEAK_TFLOPS, 2),
+           "flops_per_step": fl["total"], "steps": steps, "warmup": warmup,
+           "shape": {"batch": w.batch, "T": w.T, "heads": w.heads, "kv_heads": w.kv_heads, "causal": w.causal,
+                     "varlen": w.varlen},
+           "kernels_ms": {n: round(per[n], 4) for n in names},
+           "kernels_tflops": {n: round(fl[n] / (per[n] * 1e-3) / 1e12, 1) for n in names if fl[n] > 0}}
+    del buf
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -326,6 +403,11 @@ def main():
                     help="summarize a rocprofv3 --kernel-trace --stats run of the full bench (every path) into "
                          "profiles/ and exit")
     ap.add_argument("--profile-command", default="", help="command line recorded in the summaries")
+    ap.add_argument("--clock-settle-s", type=float, default=0.5,
+                    help="seconds of plain fp16 GEMM load before the warm-up so the timed steps start at the "
+                         "loaded clock (0: none)")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip timing the other four workloads beside the headline")
     args = ap.parse_args()
     if args.summarize_profile:
         summarize_profile(args.summarize_profile, args.workload, args.profile_command)
@@ -391,6 +473,7 @@ def main():
     # The clock snapshot (a child process, during which the GPU idles and its clock drops) is taken before
     # the warm-up, so that the timed steps follow the warm-up directly.
     state_before = None if args.headline_only else gpu_state()
+    settle = clock_settle(args.clock_settle_s) if args.clock_settle_s > 0 else None
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -565,6 +648,15 @@ def main():
                                   "tflops": round(fl["total"] / (p2_ms * 1e-3) / 1e12, 2),
                                   "backward_ms": round(p2_per[1], 4)}
 
+    # Every other workload of the path, timed the same way (the headline's
+    # launches, its step count, and at least as many warm-up steps as the
+    # headline's), each on its own buffers, freed afterwards.
+    others = None
+    if not args.headline_only and not args.no_other_workloads:
+        others = {}
+        for name in ("tiny_causal_t128", "causal_mha_t1024", "varlen_b16_t2048", "long_causal_gqa_t16384"):
+            others[name] = time_workload(name, args.steps, max(args.warmup, 3), args.block_order)
+
     if args.calibrate_copy_mb > 0:
         n = args.calibrate_copy_mb << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -585,6 +677,8 @@ def main():
         "phases": phases,
         "roofline": roofline,
     }
+    if settle is not None:
+        out["clock_settle"] = settle
     if cold is not None:
         out["cold"] = cold
     if state_before is not None or state_after is not None:
@@ -597,6 +691,8 @@ def main():
         out["dq_pass_rotated"] = dq_rotated
     if projection is not None:
         out["projection_backward"] = projection
+    if others is not None:
+        out["other_workloads"] = others
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x)
     print(json.dumps(out), flush=True)

@@ -72,6 +72,16 @@ def native():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m causal_streaming_attention_amd.build`")
+        from . import build as _build
+        try:
+            with open(_build.HASH_FILE) as f:
+                built = f.read().strip()
+        except OSError:
+            built = None
+        if built != _build.source_hash():
+            raise RuntimeError(f"{LIB_PATH} was not built from the sources beside it (source hash "
+                               f"{built} against {_build.source_hash()}): rebuild it with "
+                               "`python -m causal_streaming_attention_amd.build`")
         lib = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGS.items():
             f = getattr(lib, name)

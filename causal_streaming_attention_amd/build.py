@@ -7,6 +7,7 @@ are disabled for device code (``-packed-fp32-ops``).
 from __future__ import annotations
 
 import concurrent.futures
+import hashlib
 import os
 import subprocess
 import sys
@@ -15,6 +16,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsa.so")
+# The source hash libsa.so was built from; the binding refuses a library whose
+# hash differs from the sources beside it (a stale build).
+HASH_FILE = LIB + ".srchash"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["sa_api.cpp", "sa_forward.hip", "sa_backward.hip", "sa_query.hip"]
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -22,6 +26,20 @@ DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang"
 # are tested explicitly), so maxima need no NaN canonicalization; infinities keep their meaning.
 KERNEL_FLAGS = ["-fno-honor-nans"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
+def source_hash() -> str:
+    """Hash of everything libsa.so is built from: the sources, the headers, the C ABI header and the flags."""
+    h = hashlib.sha256()
+    names = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp", ".h")))
+    for name in names:
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    with open(os.path.join(ROOT, "include", "sa.h"), "rb") as f:
+        h.update(f.read())
+    h.update(" ".join(SOURCES + DEVICE_FLAGS + KERNEL_FLAGS + COMMON[:4]).encode())
+    return h.hexdigest()[:16]
 
 
 def _compile(src: str, out_dir: str, verbose: bool) -> str:
@@ -50,6 +68,9 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, LIB)
+    with open(HASH_FILE + ".tmp", "w") as f:
+        f.write(source_hash() + "\n")
+    os.replace(HASH_FILE + ".tmp", HASH_FILE)
     return LIB
 
 

@@ -113,3 +113,85 @@ def sample_cols(B, KV, T, n, seed, kv_list=None, lo=0):
         kv = kv_list[int(rng.integers(0, len(kv_list)))]
         ids.add((b * KV + kv) * T + int(rng.integers(lo, T)))
     return np.array(sorted(ids), dtype=np.int64)
+
+
+# The oracle's results for the named workloads, computed once per process and
+# shared by the split and two-launch tests (the oracle is deterministic).
+_REFERENCE = {}
+
+
+def workload_reference(w, x):
+    """Every output of the oracle (full forward and backward) for a workload small enough to take whole."""
+    if w.name not in _REFERENCE:
+        say(f"case {w.name}: oracle, every row and key column")
+        _REFERENCE[w.name] = full_reference(x, w.causal)
+    return _REFERENCE[w.name]
+
+
+def long_context_reference(w, x, kv_heads, n_rows):
+    """For the long-context workload: sampled rows (O, L, D, dQ) and the whole sequence's dK / dV columns of
+    the given K/V heads (key tile 0, the longest reduction, and every boosted key among them)."""
+    import oracle
+    key = (w.name, tuple(kv_heads), n_rows)
+    if key not in _REFERENCE:
+        B, H, T, KV = w.batch, w.heads, w.T, w.kv_heads
+        rows = sample_rows(B, H, T, n_rows, seed=w.seed)
+        say(f"case {w.name}: oracle rows {rows.size}")
+        D, dQ, O, L = oracle.backward_rows(x["Q"], x["K"], x["Vt"], x["dO"], s=SCALE, causal=w.causal,
+                                           seqlens=x["seqlens"], rows=rows)
+        cols = np.concatenate([np.arange((b * KV + kv) * T, (b * KV + kv + 1) * T, dtype=np.int64)
+                               for b in range(B) for kv in kv_heads])
+        say(f"case {w.name}: oracle key columns {cols.size} (K/V heads {list(kv_heads)}, whole sequence)")
+        dK, dV = oracle.backward_cols(x["Q"], x["K"], x["Vt"], x["dO"], s=SCALE, causal=w.causal,
+                                      seqlens=x["seqlens"], cols=cols)
+        _REFERENCE[key] = {"rows": rows, "D": D, "dQ": dQ, "O": O, "L": L, "cols": cols, "dK": dK, "dV": dV}
+    return _REFERENCE[key]
+
+
+def check_workload_full(w, x, got, where):
+    """Every O / L / D / dQ row and every dK / dV column against the oracle, padded rows and keys exactly 0."""
+    ref = workload_reference(w, x)
+    check_forward(got["O"], got["L"], ref["O"], ref["L"], where)
+    errs = {k: check_grad(k, got[k], ref[k], where) for k in ("dQ", "dK", "dVt")}
+    d_err = rel_l2(got["D"], ref["D"])
+    assert d_err <= 1e-2, f"{where}: D rel L2 {d_err:.2e}"
+    # each K/V head's columns on their own too, so that an error confined to one head is not averaged away
+    for b in range(w.batch):
+        for kv in range(w.kv_heads):
+            if np.linalg.norm(ref["dK"][b, kv]) > 0:
+                check_grad("dK", got["dK"][b, kv], ref["dK"][b, kv], f"{where} b={b} kv={kv}")
+                check_grad("dV", got["dVt"][b, kv], ref["dVt"][b, kv], f"{where} b={b} kv={kv}")
+    if x["seqlens"] is not None:
+        for b, n in enumerate(x["seqlens"]):
+            assert np.all(got["D"][b, :, n:] == 0) and np.all(got["dQ"][b, :, n:] == 0), where
+            assert np.all(got["dK"][b, :, n:] == 0) and np.all(got["dVt"][b, :, :, n:] == 0), where
+    say(f"{where}: full tensors: dQ {errs['dQ']:.2e} dK {errs['dK']:.2e} dV {errs['dVt']:.2e} D {d_err:.2e}")
+
+
+def check_long_context(w, x, got, where, kv_heads=(0, 5), n_rows=1024):
+    """Long-context workload: sampled rows, and the whole sequence of two K/V heads' dK / dV columns."""
+    ref = long_context_reference(w, x, kv_heads, n_rows)
+    rows = ref["rows"]
+    check_forward(got["O"].reshape(-1, 64)[rows], got["L"].reshape(-1)[rows], ref["O"], ref["L"], where)
+    check_grad("dQ", got["dQ"].reshape(-1, 64)[rows], ref["dQ"], where)
+    assert rel_l2(got["D"].reshape(-1)[rows], ref["D"]) <= 1e-2, where
+    cols = ref["cols"]
+    gK = got["dK"].reshape(-1, 64)[cols]
+    gV = np.swapaxes(got["dVt"], -1, -2).reshape(-1, 64)[cols]
+    T = w.T
+    for i, kv in enumerate(kv_heads):
+        part = slice(i * T, (i + 1) * T)
+        check_grad("dK", gK[part], ref["dK"][part], f"{where} kv={kv}")
+        check_grad("dV", gV[part], ref["dV"][part], f"{where} kv={kv}")
+        # key tile 0 (the longest walk, scheduled first) on its own
+        check_grad("dK", gK[part][:64], ref["dK"][part][:64], f"{where} kv={kv} key tile 0")
+        check_grad("dV", gV[part][:64], ref["dV"][part][:64], f"{where} kv={kv} key tile 0")
+    # every boosted key of the first head: the rows whose norm stands out (the boost is x8)
+    K0 = x["K"][0, kv_heads[0]].astype(np.float64)
+    norms = np.linalg.norm(K0, axis=1)
+    boosted = np.nonzero(norms > 4.0 * np.median(norms))[0]
+    assert boosted.size == int(round(w.boost_frac * T)), boosted.size
+    check_grad("dK", gK[:T][boosted], ref["dK"][:T][boosted], f"{where} boosted keys")
+    check_grad("dV", gV[:T][boosted], ref["dV"][:T][boosted], f"{where} boosted keys")
+    say(f"{where}: rows {rows.size}, whole-sequence dK/dV of K/V heads {list(kv_heads)}, "
+        f"{boosted.size} boosted keys")

@@ -254,3 +254,12 @@ def test_two_pass_projection_backward_rejects_bad_arguments(lib):
         assert call(bad) == sa.SA_ERR_ALIGN
     assert call(ptrs, sc=float("nan")) == sa.SA_ERR_ARGUMENT
     assert call(ptrs, width=W - 4) == sa.SA_ERR_ARGUMENT
+
+
+def test_a_library_built_from_other_sources_is_refused(monkeypatch):
+    """The binding loads libsa.so only if the source hash it was built from matches the sources beside it."""
+    from causal_streaming_attention_amd import build
+    monkeypatch.setattr(sa, "_lib", None)
+    monkeypatch.setattr(build, "source_hash", lambda: "0000000000000000")
+    with pytest.raises(RuntimeError, match="not built from the sources"):
+        sa.native()

@@ -1,9 +1,10 @@
 """GPU parity: the HIP path (through the C ABI) against the binary64 oracle.
 
 Small problems compare every output; the five named workloads run at their
-full sizes in the launch configuration the benchmark times and compare rows
-and key columns the oracle computes one by one, plus properties that hold at
-any size.  Also: bitwise determinism across repeats and block orders, grouped
+full sizes in the launch configuration the benchmark times.  Up to the
+variable-length batch every output row and key column is compared; the
+long-context workload compares 1024 sampled rows and the whole sequence of
+two K/V heads' dK / dV columns, plus properties that hold at any size.  Also: bitwise determinism across repeats and block orders, grouped
 heads against repeated heads, variable length against per-sequence runs, and
 padding that holds garbage."""
 import numpy as np
@@ -11,8 +12,8 @@ import pytest
 
 import oracle
 from causal_streaming_attention_amd.workloads import SCALE, WORKLOADS, generate, make_inputs
-from parity_util import (check_forward, check_grad, full_reference, rel_l2, run_gpu, sample_cols, sample_rows,
-                         say)
+from parity_util import (check_forward, check_grad, check_long_context, check_workload_full, full_reference,
+                         rel_l2, run_gpu, sample_cols, sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -109,27 +110,6 @@ def test_causal_mha_t1024_workload():
     _check_all(generate(w), w.causal, w.name)
 
 
-def _sampled(w, n_rows, n_cols, kv_list, col_lo=0):
-    x = generate(w)
-    say(f"case {w.name}: gpu")
-    buf, got = run_gpu(x, w.causal)
-    B, H, T, KV = w.batch, w.heads, w.T, w.kv_heads
-    rows = sample_rows(B, H, T, n_rows, seed=w.seed)
-    say(f"case {w.name}: oracle rows {rows.size}")
-    D, dQ, O, L = oracle.backward_rows(x["Q"], x["K"], x["Vt"], x["dO"], s=SCALE, causal=w.causal,
-                                       seqlens=x["seqlens"], rows=rows)
-    check_forward(got["O"].reshape(-1, 64)[rows], got["L"].reshape(-1)[rows], O, L, w.name)
-    check_grad("dQ", got["dQ"].reshape(-1, 64)[rows], dQ, w.name)
-    assert rel_l2(got["D"].reshape(-1)[rows], D) <= 1e-2
-    cols = sample_cols(B, KV, T, n_cols, seed=w.seed + 1, kv_list=kv_list, lo=col_lo)
-    say(f"case {w.name}: oracle cols {cols.size}")
-    dK, dV = oracle.backward_cols(x["Q"], x["K"], x["Vt"], x["dO"], s=SCALE, causal=w.causal,
-                                  seqlens=x["seqlens"], cols=cols)
-    check_grad("dK", got["dK"].reshape(-1, 64)[cols], dK, w.name)
-    check_grad("dV", np.swapaxes(got["dVt"], -1, -2).reshape(-1, 64)[cols], dV, w.name)
-    return x, got
-
-
 def _gradient_sums(x, got, w):
     """sum_j dK_j = 0 and sum_j dV_j = sum of the group's admitted dO rows, at full size."""
     dO = x["dO"].astype(np.float64)
@@ -145,27 +125,73 @@ def _gradient_sums(x, got, w):
             assert np.all(np.abs(dk.sum(axis=0)) <= 1e-2 * np.sqrt(np.sum(dk * dk, axis=0)) + 1e-6), (b, kv)
 
 
-def test_causal_gqa_t4096_workload_sampled():
+@pytest.mark.timeout(900)
+def test_causal_gqa_t4096_workload_full():
+    """The benchmark's workload at full size, in the benchmark's launch configuration: every output row and
+    key column against the oracle."""
     w = WORKLOADS["causal_gqa_t4096"]
-    x, got = _sampled(w, 384, 160, kv_list=[0, 7])
+    x = generate(w)
+    say(f"case {w.name}: gpu")
+    _, got = run_gpu(x, w.causal)
+    check_workload_full(w, x, got, w.name)
     _gradient_sums(x, got, w)
 
 
-def test_varlen_b16_t2048_workload_sampled():
+@pytest.mark.timeout(900)
+def test_varlen_b16_t2048_workload_full():
     w = WORKLOADS["varlen_b16_t2048"]
-    x, got = _sampled(w, 384, 128, kv_list=[3])
-    lens = x["seqlens"]
-    for b, n in enumerate(lens):
+    x = generate(w)
+    say(f"case {w.name}: gpu")
+    _, got = run_gpu(x, w.causal)
+    for b, n in enumerate(x["seqlens"]):
         assert np.all(got["O"][b, :, n:] == 0) and np.all(np.isneginf(got["L"][b, :, n:]))
-        assert np.all(got["dQ"][b, :, n:] == 0) and np.all(got["dK"][b, :, n:] == 0)
+    check_workload_full(w, x, got, w.name)
     _gradient_sums(x, got, w)
 
 
-def test_long_causal_gqa_t16384_workload_sampled():
+@pytest.mark.timeout(900)
+def test_long_causal_gqa_t16384_workload():
+    """Long context with boosted keys: 1024 sampled rows, and dK / dV over the whole sequence of two K/V
+    heads (key tile 0 and every boosted key of the first among them) against the oracle."""
     w = WORKLOADS["long_causal_gqa_t16384"]
-    # key columns from the last 768 keys: their gradients need only the rows after them
-    x, got = _sampled(w, 256, 96, kv_list=[5], col_lo=w.T - 768)
+    x = generate(w)
+    say(f"case {w.name}: gpu")
+    _, got = run_gpu(x, w.causal)
+    check_long_context(w, x, got, w.name)
     _gradient_sums(x, got, w)
+
+
+def test_the_pages_calls_batch1_causal():
+    """sa_forward and sa_backward, the pages' own argument lists (batch 1, causal), against the oracle on
+    the causal_mha_t1024 workload and bitwise against the general entry points, with grouped heads too."""
+    import torch
+    import causal_streaming_attention_amd as sa
+    from parity_util import C
+    for name in ("causal_mha_t1024", "causal_gqa_t4096"):
+        w = WORKLOADS[name]
+        x = generate(w)
+        say(f"case pages' calls {w.name}")
+        buf, via_ex = run_gpu(x, True)
+        T, H, KV = w.T, w.heads, w.kv_heads
+        f16, f32 = torch.float16, torch.float32
+        O = torch.empty((1, T, H * 64), dtype=f16, device="cuda")
+        L = torch.empty((1, H, T), dtype=f32, device="cuda")
+        D = torch.empty((1, H, T), dtype=f32, device="cuda")
+        dQ = torch.empty((1, H, T, 64), dtype=f32, device="cuda")
+        dK = torch.empty((1, KV, T, 64), dtype=f32, device="cuda")
+        dVt = torch.empty((1, KV, 64, T), dtype=f32, device="cuda")
+        dS = torch.empty(buf.ws_bytes, dtype=torch.uint8, device="cuda")
+        sa.sa_forward(buf.Q, buf.K, buf.Vt, O, L, C, T, H, KV)
+        sa.sa_backward(buf.dO, O, L, D, dS, buf.ws_bytes, buf.Q, buf.K, buf.Vt, C, SCALE, T, H, KV, dQ, dK, dVt)
+        torch.cuda.synchronize()
+        got = {"O": O.view(1, T, H, 64).permute(0, 2, 1, 3).float().cpu().numpy().astype(np.float64),
+               "L": L.cpu().numpy().astype(np.float64), "D": D.cpu().numpy().astype(np.float64),
+               "dQ": dQ.cpu().numpy().astype(np.float64), "dK": dK.cpu().numpy().astype(np.float64),
+               "dVt": dVt.cpu().numpy().astype(np.float64)}
+        for k in got:
+            assert np.array_equal(got[k], via_ex[k]), f"{name}: {k} differs from the general entry point"
+        if name == "causal_mha_t1024":
+            check_workload_full(w, x, got, f"{name} (pages' calls)")
 
 
 def test_determinism_and_block_order():

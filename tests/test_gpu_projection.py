@@ -1,7 +1,7 @@
 """GPU parity of the backward that stores dQ, dK and dV straight into a fused
 QKV projection's token-major gradient (sa_backward_projection): the binary32
 slices equal the split path's dQ, dK, dV bitwise (same arithmetic), the
-bfloat16 copies are their round-to-nearest-even values bit for bit, the slices
+bfloat16 copies equal torch's own bfloat16 conversion of them bit for bit, the slices
 match the oracle's layout of its own gradients, columns outside the slices are
 untouched, and padded rows are zero."""
 import numpy as np
@@ -20,9 +20,10 @@ SENT16 = 0x3FC0      # bfloat16 1.5
 EXTRA = 16           # columns past the three slices, never written
 
 
-def _rne_bf16(x32):
-    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+def _torch_bf16(x32):
+    """torch's own float32 -> bfloat16 conversion (round to nearest even), as raw bits."""
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
 
 
 def _projection(buf, H, KV, two_pass=False):
@@ -59,7 +60,7 @@ def _check(x, causal, H, KV, name, with_oracle=True):
     want32 = oracle.projection_slices(got["dQ"], got["dK"], got["dVt"], width, qc, kc, vc).astype(np.float32)
     used = slice(0, vc + 64 * KV)
     assert np.array_equal(g32[:, :, used], want32[:, :, used]), f"{name}: binary32 slices differ from the planes"
-    assert np.array_equal(g16[:, :, used], _rne_bf16(g32[:, :, used])), f"{name}: bfloat16 copies not RNE"
+    assert np.array_equal(g16[:, :, used], _torch_bf16(g32[:, :, used])), f"{name}: bfloat16 copies not RNE"
     assert np.all(g32[:, :, vc + 64 * KV:] == SENT32) and np.all(g16[:, :, vc + 64 * KV:] == SENT16), \
         f"{name}: columns past the slices were written"
     if x["seqlens"] is not None:
@@ -108,7 +109,7 @@ def test_two_pass_projection_small(name, B, T, H, KV, causal, seqlens):
     want32 = oracle.projection_slices(got["dQ"], got["dK"], got["dVt"], width, qc, kc, vc).astype(np.float32)
     used = slice(0, vc + 64 * KV)
     assert np.array_equal(g32[:, :, used], want32[:, :, used]), f"{name}: binary32 slices differ from the planes"
-    assert np.array_equal(g16[:, :, used], _rne_bf16(g32[:, :, used])), f"{name}: bfloat16 copies not RNE"
+    assert np.array_equal(g16[:, :, used], _torch_bf16(g32[:, :, used])), f"{name}: bfloat16 copies not RNE"
     assert np.all(g32[:, :, vc + 64 * KV:] == SENT32) and np.all(g16[:, :, vc + 64 * KV:] == SENT16)
     if seqlens is not None:
         for b, n in enumerate(seqlens):

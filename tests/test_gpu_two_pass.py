@@ -5,10 +5,9 @@ Every test here needs an MI355X."""
 import numpy as np
 import pytest
 
-import oracle
 from causal_streaming_attention_amd.workloads import SCALE, WORKLOADS, generate, make_inputs
-from parity_util import (check_forward, check_grad, full_reference, rel_l2, run_gpu, sample_cols, sample_rows,
-                         say)
+from parity_util import (check_forward, check_grad, check_long_context, check_workload_full, full_reference,
+                         rel_l2, run_gpu, say)
 from test_gpu_parity import SMALL, _gradient_sums, _structured_scores
 
 pytestmark = pytest.mark.gpu
@@ -52,39 +51,35 @@ def test_two_pass_causal_mha_t1024_workload():
     _check_all(generate(w), w.causal, w.name)
 
 
-def _sampled(w, n_rows, n_cols, kv_list, col_lo=0):
+@pytest.mark.timeout(900)
+def test_two_pass_causal_gqa_t4096_workload_full():
+    w = WORKLOADS["causal_gqa_t4096"]
     x = generate(w)
     say(f"case two-pass {w.name}: gpu")
     _, got = run_gpu(x, w.causal, path=PATH)
-    B, H, T, KV = w.batch, w.heads, w.T, w.kv_heads
-    rows = sample_rows(B, H, T, n_rows, seed=w.seed + 10)
-    say(f"case two-pass {w.name}: oracle rows {rows.size}")
-    D, dQ, O, L = oracle.backward_rows(x["Q"], x["K"], x["Vt"], x["dO"], s=SCALE, causal=w.causal,
-                                       seqlens=x["seqlens"], rows=rows)
-    check_forward(got["O"].reshape(-1, 64)[rows], got["L"].reshape(-1)[rows], O, L, w.name)
-    check_grad("dQ", got["dQ"].reshape(-1, 64)[rows], dQ, w.name)
-    assert rel_l2(got["D"].reshape(-1)[rows], D) <= 1e-2
-    cols = sample_cols(B, KV, T, n_cols, seed=w.seed + 11, kv_list=kv_list, lo=col_lo)
-    say(f"case two-pass {w.name}: oracle cols {cols.size}")
-    dK, dV = oracle.backward_cols(x["Q"], x["K"], x["Vt"], x["dO"], s=SCALE, causal=w.causal,
-                                  seqlens=x["seqlens"], cols=cols)
-    check_grad("dK", got["dK"].reshape(-1, 64)[cols], dK, w.name)
-    check_grad("dV", np.swapaxes(got["dVt"], -1, -2).reshape(-1, 64)[cols], dV, w.name)
-    return x, got
-
-
-def test_two_pass_causal_gqa_t4096_workload_sampled():
-    w = WORKLOADS["causal_gqa_t4096"]
-    x, got = _sampled(w, 384, 160, kv_list=[1, 6])
+    check_workload_full(w, x, got, f"{w.name} two-pass")
     _gradient_sums(x, got, w)
 
 
-def test_two_pass_varlen_b16_t2048_workload_sampled():
+@pytest.mark.timeout(900)
+def test_two_pass_varlen_b16_t2048_workload_full():
     w = WORKLOADS["varlen_b16_t2048"]
-    x, got = _sampled(w, 384, 128, kv_list=[9])
-    for b, n in enumerate(x["seqlens"]):
-        assert np.all(got["dQ"][b, :, n:] == 0) and np.all(got["D"][b, :, n:] == 0)
-        assert np.all(got["dK"][b, :, n:] == 0) and np.all(got["dVt"][b, :, :, n:] == 0)
+    x = generate(w)
+    say(f"case two-pass {w.name}: gpu")
+    _, got = run_gpu(x, w.causal, path=PATH)
+    check_workload_full(w, x, got, f"{w.name} two-pass")
+    _gradient_sums(x, got, w)
+
+
+@pytest.mark.timeout(900)
+def test_two_pass_long_causal_gqa_t16384_workload():
+    """The two-launch backward exists to give long context O(T) memory: at T = 16384 with boosted keys,
+    the same rows and whole-sequence key columns as the split path's test."""
+    w = WORKLOADS["long_causal_gqa_t16384"]
+    x = generate(w)
+    say(f"case two-pass {w.name}: gpu")
+    _, got = run_gpu(x, w.causal, path=PATH)
+    check_long_context(w, x, got, f"{w.name} two-pass")
     _gradient_sums(x, got, w)
 
 
