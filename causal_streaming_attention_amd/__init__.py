@@ -22,7 +22,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsa.so")
 _lib = None
 
-SA_OK, SA_ERR_SHAPE, SA_ERR_NULL, SA_ERR_ALIGN, SA_ERR_WORKSPACE, SA_ERR_ARGUMENT, SA_ERR_DEVICE = range(7)
+(SA_OK, SA_ERR_SHAPE, SA_ERR_NULL, SA_ERR_ALIGN, SA_ERR_WORKSPACE, SA_ERR_ARGUMENT, SA_ERR_DEVICE,
+ SA_ERR_TOO_LARGE) = range(8)
+SA_STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class SaShape(ctypes.Structure):
@@ -61,6 +63,7 @@ _SIGS = {
                                              _V]),
     "sa_query_pass": (_I, [_SP, _V, _V, _V, _V, _V, _V, _F, _F, _V, _V, _V]),
     "sa_backward_two_pass": (_I, [_SP, _V, _V, _V, _V, _V, _V, _V, _F, _F, _V, _V, _V, _V]),
+    "sa_backward_static": (_I, [_SP, _V, _V, _V, _V, _V, _V, _V, _F, _F, _V, _V, _V, _V]),
     "sa_status_string": (ctypes.c_char_p, [_I]),
 }
 
@@ -164,6 +167,13 @@ def sa_backward_ex(shape, dO, O, L, D, dS, dS_bytes, Q, K, Vt, c, s, dQ, dK, dVt
     _check(native().sa_backward_ex(ctypes.byref(shape), _ptr(dO), _ptr(O), _ptr(L), _ptr(D), _ptr(dS),
                                    dS_bytes, _ptr(Q), _ptr(K), _ptr(Vt), c, s, _ptr(dQ), _ptr(dK), _ptr(dVt),
                                    _stream(stream)), "sa_backward_ex")
+
+
+def sa_backward_static(shape, dO, O, L, D, Q, K, Vt, c, s, dQ, dK, dVt, stream=None):
+    """The split backward with the library's static dS scratch (no workspace argument, nothing allocated)."""
+    _check(native().sa_backward_static(ctypes.byref(shape), _ptr(dO), _ptr(O), _ptr(L), _ptr(D), _ptr(Q), _ptr(K),
+                                       _ptr(Vt), c, s, _ptr(dQ), _ptr(dK), _ptr(dVt), _stream(stream)),
+           "sa_backward_static")
 
 
 def sa_row_terms(shape, dO, O, D, stream=None):

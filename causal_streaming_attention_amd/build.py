@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libsa.so")
 # hash differs from the sources beside it (a stale build).
 HASH_FILE = LIB + ".srchash"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["sa_api.cpp", "sa_forward.hip", "sa_backward.hip", "sa_query.hip"]
+SOURCES = ["sa_api.cpp", "sa_forward.hip", "sa_backward.hip", "sa_query.hip", "sa_static.hip"]
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # The kernels never form a NaN from finite inputs (masked scores are selected to -inf, empty rows
 # are tested explicitly), so maxima need no NaN canonicalization; infinities keep their meaning.

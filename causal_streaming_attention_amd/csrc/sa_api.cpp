@@ -229,6 +229,7 @@ const char* sa_status_string(int status) {
         case SA_ERR_WORKSPACE: return "dS workspace smaller than sa_backward_workspace_bytes";
         case SA_ERR_ARGUMENT: return "scale c or s is not finite and positive, or a bad projection width";
         case SA_ERR_DEVICE: return "a HIP kernel launch failed";
+        case SA_ERR_TOO_LARGE: return "the dS workspace exceeds the library's static scratch (SA_STATIC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }

@@ -5,7 +5,9 @@
  * device pointers, sizes and a HIP stream (as void*, NULL = the default
  * stream), enqueues its kernels on that stream and returns without
  * synchronising.  The library never allocates, frees or copies memory of its
- * own: the caller owns every buffer.  No exception crosses the boundary and
+ * own: the caller owns every buffer, apart from the static device array
+ * behind sa_backward_static (SA_STATIC_SCRATCH_BYTES per GPU, held by the
+ * loaded code object until the process ends).  No exception crosses the boundary and
  * the process is never aborted; every failure is a returned status, checked
  * before anything is launched (except SA_ERR_DEVICE, reported by the launch).
  *
@@ -68,8 +70,15 @@ typedef enum sa_status {
     SA_ERR_ALIGN = 3,      /* a pointer is not 16-byte aligned (seqlens: 4-byte) */
     SA_ERR_WORKSPACE = 4,  /* dS_bytes < sa_backward_workspace_bytes(shape) */
     SA_ERR_ARGUMENT = 5,   /* c or s not finite and positive */
-    SA_ERR_DEVICE = 6      /* a HIP launch failed (read, and so cleared, by hipGetLastError) */
+    SA_ERR_DEVICE = 6,     /* a HIP launch failed (read, and so cleared, by hipGetLastError) */
+    SA_ERR_TOO_LARGE = 7   /* sa_backward_static: the shape's dS workspace exceeds
+                              SA_STATIC_SCRATCH_BYTES */
 } sa_status;
+
+/* Size of the library's static device scratch that sa_backward_static uses
+ * as its dS workspace (held on every GPU the library runs on, for the life of
+ * the process). */
+#define SA_STATIC_SCRATCH_BYTES (64u << 20)
 
 /*
  * Problem shape.  Admission (the pages' admission predicate for the grouped
@@ -266,6 +275,29 @@ sa_status sa_backward_two_pass_projection(const sa_shape* shape, const void* dO,
                                           float* D, const void* Q, const void* K, const void* Vt, float c, float s,
                                           float* dQ32, void* dQ16, float* dK32, void* dK16, float* dV32, void* dV16,
                                           int width, void* stream);
+
+/*
+ * The split backward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): sa_backward_ex's three launches with the
+ * dS workspace in a static device array of SA_STATIC_SCRATCH_BYTES that the
+ * library holds on each GPU until the process ends.  The call itself
+ * allocates nothing.
+ *   Arguments: as sa_backward_ex without dS and dS_bytes.
+ *   Limit: a shape whose sa_backward_workspace_bytes exceeds
+ *          SA_STATIC_SCRATCH_BYTES returns SA_ERR_TOO_LARGE (checked before
+ *          anything else touches the GPU), e.g. batch 1, T = 1024, 8 heads
+ *          needs 8.9 MB; T = 4096, 32 heads needs 545 MB and is refused.
+ *   Results: bitwise equal to sa_backward_ex's for the same inputs.
+ *   Concurrency: every call on one GPU shares that GPU's array; calls that
+ *          overlap on one GPU (other streams, other host threads) race.  Calls
+ *          on one stream run in order and are safe.
+ *   Errors: as sa_backward_ex; SA_ERR_DEVICE also if the array's device
+ *          address cannot be looked up on the current device.
+ */
+sa_status sa_backward_static(const sa_shape* shape, const void* dO, const void* O, const float* L, float* D,
+                             const void* Q, const void* K, const void* Vt, float c, float s,
+                             float* dQ, float* dK, float* dVt, void* stream);
 
 /* Static text for a status value ("unknown status" for anything else). */
 const char* sa_status_string(int status);

@@ -263,3 +263,23 @@ def test_a_library_built_from_other_sources_is_refused(monkeypatch):
     monkeypatch.setattr(build, "source_hash", lambda: "0000000000000000")
     with pytest.raises(RuntimeError, match="not built from the sources"):
         sa.native()
+
+
+def test_static_scratch_backward_rejects_before_touching_the_gpu(lib):
+    """sa_backward_static checks shape, pointers, scales and its size limit before any HIP call."""
+    P = 256
+    big = shape(batch=1, T=4096, heads=32, kv=8)
+    assert sa.sa_backward_workspace_bytes(big) > sa.SA_STATIC_SCRATCH_BYTES
+    args = [P] * 7 + [sa.base2_scale(0.125), 0.125] + [P] * 3 + [None]
+    f = lib.sa_backward_static
+    assert f(ctypes.byref(big), *args) == sa.SA_ERR_TOO_LARGE
+    assert f(ctypes.byref(shape(T=100)), *args) == sa.SA_ERR_SHAPE
+    bad = list(args)
+    bad[0] = None
+    assert f(ctypes.byref(shape()), *bad) == sa.SA_ERR_NULL
+    bad[0] = P + 8
+    assert f(ctypes.byref(shape()), *bad) == sa.SA_ERR_ALIGN
+    bad = list(args)
+    bad[7] = float("nan")
+    assert f(ctypes.byref(shape()), *bad) == sa.SA_ERR_ARGUMENT
+    assert "static scratch" in sa.sa_status_string(sa.SA_ERR_TOO_LARGE)
