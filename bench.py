@@ -406,6 +406,8 @@ def main():
     ap.add_argument("--clock-settle-s", type=float, default=0.5,
                     help="seconds of plain fp16 GEMM load before the warm-up so the timed steps start at the "
                          "loaded clock (0: none)")
+    ap.add_argument("--chunk-mib", type=int, nargs="*", default=[128, 256],
+                    help="workspace sizes (MiB) at which the chunked split backward is timed beside the headline")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip timing the other four workloads beside the headline")
     args = ap.parse_args()
@@ -648,6 +650,33 @@ def main():
                                   "tflops": round(fl["total"] / (p2_ms * 1e-3) / 1e12, 2),
                                   "backward_ms": round(p2_per[1], 4)}
 
+    # The chunked split backward (sa_backward_chunked): the key and dQ passes
+    # in query-row chunks over a workspace of a few sizes, so that one chunk's
+    # dS at a time is written and read back, timed like the headline.
+    chunked = None
+    if not args.headline_only:
+        chunked = {}
+        for mib in args.chunk_mib:
+            ws_bytes = mib << 20
+            if ws_bytes < sa.sa_backward_chunked_min_bytes(sh):
+                continue
+            ws_bytes = min(ws_bytes, buf.ws_bytes)
+
+            def step_chunked(ev=None, ws_bytes=ws_bytes):
+                if ev: ev[0].record(stream)
+                sa.sa_forward_ex(sh, buf.Q, buf.K, buf.Vt, buf.O, buf.L, c, stream)
+                if ev: ev[1].record(stream)
+                sa.sa_backward_chunked(sh, buf.dO, buf.O, buf.L, buf.D, buf.dS, ws_bytes, buf.Q, buf.K, buf.Vt, c,
+                                       SCALE, buf.dQ, buf.dK, buf.dVt, stream)
+                if ev: ev[2].record(stream)
+
+            for _ in range(args.warmup):
+                step_chunked()
+            ch_ms, ch_per, _ = timed(step_chunked, 2)
+            chunked[f"{mib}MiB"] = {"ms_per_step": round(ch_ms, 4),
+                                    "tflops": round(fl["total"] / (ch_ms * 1e-3) / 1e12, 2),
+                                    "backward_ms": round(ch_per[1], 4), "workspace_bytes": ws_bytes}
+
     # Every other workload of the path, timed the same way (the headline's
     # launches, its step count, and at least as many warm-up steps as the
     # headline's), each on its own buffers, freed afterwards.
@@ -691,6 +720,8 @@ def main():
         out["dq_pass_rotated"] = dq_rotated
     if projection is not None:
         out["projection_backward"] = projection
+    if chunked is not None:
+        out["chunked_backward"] = chunked
     if others is not None:
         out["other_workloads"] = others
     if not args.no_cpu_baseline:

@@ -64,6 +64,8 @@ _SIGS = {
     "sa_query_pass": (_I, [_SP, _V, _V, _V, _V, _V, _V, _F, _F, _V, _V, _V]),
     "sa_backward_two_pass": (_I, [_SP, _V, _V, _V, _V, _V, _V, _V, _F, _F, _V, _V, _V, _V]),
     "sa_backward_static": (_I, [_SP, _V, _V, _V, _V, _V, _V, _V, _F, _F, _V, _V, _V, _V]),
+    "sa_backward_chunked": (_I, [_SP, _V, _V, _V, _V, _V, _Z, _V, _V, _V, _F, _F, _V, _V, _V, _V]),
+    "sa_backward_chunked_min_bytes": (_Z, [_SP]),
     "sa_status_string": (ctypes.c_char_p, [_I]),
 }
 
@@ -167,6 +169,16 @@ def sa_backward_ex(shape, dO, O, L, D, dS, dS_bytes, Q, K, Vt, c, s, dQ, dK, dVt
     _check(native().sa_backward_ex(ctypes.byref(shape), _ptr(dO), _ptr(O), _ptr(L), _ptr(D), _ptr(dS),
                                    dS_bytes, _ptr(Q), _ptr(K), _ptr(Vt), c, s, _ptr(dQ), _ptr(dK), _ptr(dVt),
                                    _stream(stream)), "sa_backward_ex")
+
+
+def sa_backward_chunked(shape, dO, O, L, D, dS, dS_bytes, Q, K, Vt, c, s, dQ, dK, dVt, stream=None):
+    _check(native().sa_backward_chunked(ctypes.byref(shape), _ptr(dO), _ptr(O), _ptr(L), _ptr(D), _ptr(dS),
+                                        dS_bytes, _ptr(Q), _ptr(K), _ptr(Vt), c, s, _ptr(dQ), _ptr(dK), _ptr(dVt),
+                                        _stream(stream)), "sa_backward_chunked")
+
+
+def sa_backward_chunked_min_bytes(shape) -> int:
+    return int(native().sa_backward_chunked_min_bytes(ctypes.byref(shape)))
 
 
 def sa_backward_static(shape, dO, O, L, D, Q, K, Vt, c, s, dQ, dK, dVt, stream=None):

@@ -173,6 +173,25 @@ sa_status sa_backward_ex(const sa_shape* shape, const void* dO, const void* O, c
     return from_hip(sa::launch_dq_pass(sh, K, dS, s, dQ, strm));
 }
 
+size_t sa_backward_chunked_min_bytes(const sa_shape* shape) {
+    if (sa_check_shape(shape) != SA_OK) return 0;
+    return sa::min_chunk_bytes(to_shape(shape));
+}
+
+sa_status sa_backward_chunked(const sa_shape* shape, const void* dO, const void* O, const float* L, float* D,
+                              void* dS, size_t dS_bytes, const void* Q, const void* K, const void* Vt, float c,
+                              float s, float* dQ, float* dK, float* dVt, void* stream) {
+    sa_status st = sa_check_shape(shape);
+    if (st != SA_OK) return st;
+    if ((st = check_ptrs({dO, O, L, D, dS, Q, K, Vt, dQ, dK, dVt})) != SA_OK) return st;
+    if (dS_bytes < sa_backward_chunked_min_bytes(shape)) return SA_ERR_WORKSPACE;
+    if (!scale_ok(c) || !scale_ok(s)) return SA_ERR_ARGUMENT;
+    const sa::Shape sh = to_shape(shape);
+    hipStream_t strm = (hipStream_t)stream;
+    if ((st = from_hip(sa::launch_row_terms(sh, dO, O, D, strm))) != SA_OK) return st;
+    return from_hip(sa::launch_key_dq_chunked(sh, Q, K, Vt, dO, L, D, dS, dS_bytes, c, s, dQ, dK, dVt, strm));
+}
+
 sa_status sa_backward(const void* dO, const void* O, const float* L, float* D, void* dS, size_t dS_bytes,
                       const void* Q, const void* K, const void* Vt, float c, float s, int T, int heads,
                       int kv_heads, float* dQ, float* dK, float* dVt, void* stream) {
@@ -226,7 +245,7 @@ const char* sa_status_string(int status) {
         case SA_ERR_SHAPE: return "shape fails admission (T multiple of 64, heads divisible by kv_heads, limits)";
         case SA_ERR_NULL: return "a required pointer is NULL";
         case SA_ERR_ALIGN: return "a pointer is not 16-byte aligned (seqlens: 4-byte)";
-        case SA_ERR_WORKSPACE: return "dS workspace smaller than sa_backward_workspace_bytes";
+        case SA_ERR_WORKSPACE: return "dS workspace too small (sa_backward_workspace_bytes; sa_backward_chunked_min_bytes for the chunked backward)";
         case SA_ERR_ARGUMENT: return "scale c or s is not finite and positive, or a bad projection width";
         case SA_ERR_DEVICE: return "a HIP kernel launch failed";
         case SA_ERR_TOO_LARGE: return "the dS workspace exceeds the library's static scratch (SA_STATIC_SCRATCH_BYTES)";

@@ -15,6 +15,7 @@
 // dV is folded into the key pass (one workgroup per K/V head and key tile,
 // its query heads in parallel wave pairs, summed through LDS in a fixed
 // order), so there are no atomics and no partial-gradient planes.
+#include <algorithm>
 #include <type_traits>
 
 #include "sa_device.h"
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     const half_t* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ D,
     half_t* __restrict__ dS, float* __restrict__ dK, float* __restrict__ dVt,
     const int32_t* __restrict__ seqlens, float c, float s, int T, int H, int KV, int nkt, int BKV,
-    int block_order, long long tiles_per_head, int v_rows, ProjectionOut kproj, ProjectionOut vproj) {
+    int block_order, Chunk ch, int v_rows, ProjectionOut kproj, ProjectionOut vproj) {
     constexpr int kThreads = 128 * GW;
     __shared__ __attribute__((aligned(16))) char smem[KeyLds<GW>::bytes];
 
@@ -178,10 +179,11 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     const int kbase = kt * kTile + 32 * khalf;  // this wave's first key
     const int key = kbase + l32;                // this lane's key
 
-    // Query sub-tiles walked: whole 64-row tiles that the dQ pass reads.
+    // Query sub-tiles walked: whole 64-row tiles that the dQ pass reads, in
+    // the chunk's query tiles [ch.q_lo, ch.q_hi).
     const int qlimit = VARLEN ? ((len + kTile - 1) / kTile) * kTile : T;
-    const int sub_hi = qlimit / kSubRows;
-    const int sub_lo = CAUSAL ? 2 * kt : 0;
+    const int sub_hi = min(qlimit / kSubRows, 2 * ch.q_hi);
+    const int sub_lo = CAUSAL ? max(2 * kt, 2 * ch.q_lo) : 2 * ch.q_lo;
     const bool tile_live = !VARLEN || kt * kTile < len;
     const int n_sub = tile_live ? max(0, sub_hi - sub_lo) : 0;
     const int n_items = n_sub * (G / GW);
@@ -421,8 +423,9 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
         // reuses nor stalls the walk behind L2 write-backs.
         if (store_ds) {
             const int qt = sub >> 1;
-            const size_t tile = CAUSAL ? (size_t)qt * (qt + 1) / 2 + kt : (size_t)qt * (T / kTile) + kt;
-            half_t* dsp = dS + (((size_t)b * H + head) * (size_t)tiles_per_head + tile) * (kTile * kTile) +
+            const size_t tile = (CAUSAL ? (size_t)qt * (qt + 1) / 2 + kt : (size_t)qt * (T / kTile) + kt) -
+                                (size_t)ch.tile0;
+            half_t* dsp = dS + (((size_t)b * H + head) * (size_t)ch.tph + tile) * (kTile * kTile) +
                           (size_t)(2 * (sub & 1) + khalf) * 1024 + 8 * lane;
             __builtin_nontemporal_store(half8_from_words(wd[0], wd[1], wd[2], wd[3]), (half8*)dsp);
             __builtin_nontemporal_store(half8_from_words(wd[4], wd[5], wd[6], wd[7]), (half8*)(dsp + 512));
@@ -458,8 +461,12 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     // token-major gradient takes K/V head kv's values at columns 64 kv + d of
     // the slice the pointers name, in binary32 and rounded to bfloat16.
     const size_t tok_row0 = (size_t)b * T + (size_t)kt * kTile;
-    auto store_proj = [&](const ProjectionOut& pr, int kk, int d4, const f32x4& v) {
+    // With ch.accumulate (every query-row chunk after the first), the sums
+    // are added to what the outputs hold: the earlier chunks' dK and dV.
+    const bool acc = ch.accumulate != 0;
+    auto store_proj = [&](const ProjectionOut& pr, int kk, int d4, f32x4 v) {
         const size_t at = (tok_row0 + kk) * (size_t)pr.width + kHeadDim * kv + d4;
+        if (acc) v += *(const f32x4*)(pr.f32 + at);
         *(f32x4*)(pr.f32 + at) = v;
         *(uint2*)(pr.b16 + at) = pack_bf16x4(v[0], v[1], v[2], v[3]);
     };
@@ -472,8 +479,13 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
 #pragma unroll
         for (int g = 1; g < GW; ++g) v += *(const f32x4*)&red[(g * 64 + kk) * kRedRow + d4];
         v *= s;
-        if (proj) store_proj(kproj, kk, d4, v);
-        else *(f32x4*)(dK + (key_row0 + kk) * kHeadDim + d4) = v;
+        if (proj) {
+            store_proj(kproj, kk, d4, v);
+        } else {
+            f32x4* out = (f32x4*)(dK + (key_row0 + kk) * kHeadDim + d4);
+            if (acc) v += *out;
+            *out = v;
+        }
     }
     __syncthreads();
     to_lds(dvacc0, dvacc1);
@@ -484,8 +496,13 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
             f32x4 v = *(const f32x4*)&red[kk * kRedRow + d4];
 #pragma unroll
             for (int g = 1; g < GW; ++g) v += *(const f32x4*)&red[(g * 64 + kk) * kRedRow + d4];
-            if (proj) store_proj(vproj, kk, d4, v);
-            else *(f32x4*)(dVt + (key_row0 + kk) * kHeadDim + d4) = v;
+            if (proj) {
+                store_proj(vproj, kk, d4, v);
+            } else {
+                f32x4* out = (f32x4*)(dVt + (key_row0 + kk) * kHeadDim + d4);
+                if (acc) v += *out;
+                *out = v;
+            }
         }
         return;
     }
@@ -499,7 +516,9 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
             for (int g = 1; g < GW; ++g) a += red[(g * 64 + k4 + e) * kRedRow + d];
             v[e] = a;
         }
-        *(f32x4*)(dVt + (((size_t)b * KV + kv) * kHeadDim + d) * T + (size_t)kt * kTile + k4) = v;
+        f32x4* out = (f32x4*)(dVt + (((size_t)b * KV + kv) * kHeadDim + d) * T + (size_t)kt * kTile + k4);
+        if (acc) v += *out;
+        *out = v;
     }
 }
 
@@ -558,8 +577,7 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
                                                                float* __restrict__ dQ,
                                                                const int32_t* __restrict__ seqlens, float s,
                                                                int T, int H, int KV, int n_qblk, int BH,
-                                                               int block_order, long long tiles_per_head,
-                                                               DqEpilogue rot) {
+                                                               int block_order, Chunk ch, DqEpilogue rot) {
     __shared__ __attribute__((aligned(16))) half_t lds[kDqDepth][kKTileHalves];  // K tiles
     __shared__ __attribute__((aligned(16))) half_t dsl[kDqWaves][kDsBlockHalves];  // each wave's dS block
 
@@ -568,15 +586,18 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
     // Block -> (batch*head, query blocks).  Order 0: the pair (n - 1 - p, p),
     // whose causal walks add up to the same length, with the heads of one kv
     // head kept on one XCD.  Order 1: one query block per block, plain order.
+    // The chunk's query blocks are blk_lo .. blk_lo + n_qblk - 1 (all of them
+    // when the backward is not chunked).
+    const int blk_lo = ch.q_lo / 2;
     int bh, n_items, items[2];
     if (block_order == 0) {
         int pair;
         pair_schedule((int)blockIdx.x, (BH / H) * KV, H / KV, pair, bh);
-        items[0] = n_qblk - 1 - pair;
-        items[1] = pair;
-        n_items = pair < items[0] ? 2 : 1;
+        items[0] = blk_lo + n_qblk - 1 - pair;
+        items[1] = blk_lo + pair;
+        n_items = pair < n_qblk - 1 - pair ? 2 : 1;
     } else {
-        items[0] = items[1] = (int)(blockIdx.x % n_qblk);
+        items[0] = items[1] = blk_lo + (int)(blockIdx.x % n_qblk);
         bh = (int)(blockIdx.x / n_qblk);
         n_items = 1;
     }
@@ -636,9 +657,10 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
         // tiles up to kt_last.
         const int qt_l = min(qt_w, nt - 1);
         const int kt_last = CAUSAL ? qt_l : nt - 1;
-        const half_t* dSw = dS + ((size_t)b * H + h) * (size_t)tiles_per_head * (kTile * kTile) +
+        const half_t* dSw = dS + ((size_t)b * H + h) * (size_t)ch.tph * (kTile * kTile) +
                             (size_t)(2 * qh) * 1024 + 8 * lane +
-                            (CAUSAL ? (size_t)qt_l * (qt_l + 1) / 2 : (size_t)qt_l * nt) * (kTile * kTile);
+                            ((CAUSAL ? (size_t)qt_l * (qt_l + 1) / 2 : (size_t)qt_l * nt) - (size_t)ch.tile0) *
+                                (kTile * kTile);
         auto load_s = [&](int kt, half8 (&dst)[4]) {
             const half_t* t_ = dSw + (size_t)min(kt, kt_last) * (kTile * kTile);
             dst[0] = gload16_stream_async(t_);
@@ -819,10 +841,10 @@ template <bool CAUSAL, bool VARLEN>
 void launch_key_gw(int GW, dim3 grid, hipStream_t stream, const half_t* Q, const half_t* K, const half_t* Vt,
                    const half_t* dO, const float* L, const float* D, half_t* dS, float* dK, float* dVt,
                    const int32_t* seqlens, float c, float s, int T, int H, int KV, int nkt, int BKV, int order,
-                   long long tph, int v_rows, const ProjectionOut& kproj, const ProjectionOut& vproj) {
+                   const Chunk& ch, int v_rows, const ProjectionOut& kproj, const ProjectionOut& vproj) {
 #define SA_KEY_LAUNCH(gw)                                                                                    \
     hipLaunchKernelGGL((sa_key_kernel<CAUSAL, VARLEN, gw>), grid, dim3(128 * gw), 0, stream, Q, K, Vt, dO, L, \
-                       D, dS, dK, dVt, seqlens, c, s, T, H, KV, nkt, BKV, order, tph, v_rows, kproj, vproj)
+                       D, dS, dK, dVt, seqlens, c, s, T, H, KV, nkt, BKV, order, ch, v_rows, kproj, vproj)
     switch (GW) {
         case 4: SA_KEY_LAUNCH(4); break;
         case 3: SA_KEY_LAUNCH(3); break;
@@ -864,18 +886,26 @@ hipError_t launch_row_terms(const Shape& sh, const void* dO, const void* O, floa
     return hipGetLastError();
 }
 
-hipError_t launch_key_pass_to(const Shape& sh, const void* Q, const void* K, const void* Vt, const void* dO,
-                              const float* L, const float* D, void* dS, float c, float s, float* dK, float* dVt,
-                              const ProjectionOut& kproj, const ProjectionOut& vproj, hipStream_t stream) {
-    const int nkt = sh.T / kTile, BKV = sh.batch * sh.kv_heads;
+// Key tiles a chunk's key pass launches: causal, only those below the
+// chunk's last query tile (the later ones are finished by earlier chunks).
+int chunk_key_tiles(const Shape& sh, const Chunk& ch) {
+    const int nt = sh.T / kTile;
+    return sh.causal ? min(ch.q_hi, nt) : nt;
+}
+
+hipError_t launch_key_pass_chunk(const Shape& sh, const Chunk& ch, const void* Q, const void* K, const void* Vt,
+                                 const void* dO, const float* L, const float* D, void* dS, float c, float s,
+                                 float* dK, float* dVt, const ProjectionOut& kproj, const ProjectionOut& vproj,
+                                 hipStream_t stream) {
+    const int nkt = chunk_key_tiles(sh, ch), BKV = sh.batch * sh.kv_heads;
+    if (nkt <= 0) return hipSuccess;
     const int GW = key_gw(sh.heads / sh.kv_heads);
-    dim3 grid((unsigned)key_pass_blocks(sh));
-    const long long tph = (long long)ds_tiles_per_head(sh);
+    dim3 grid((unsigned)((size_t)BKV * nkt));
     auto go = [&](auto causal_tag, auto varlen_tag) {
         constexpr bool C = decltype(causal_tag)::value, V = decltype(varlen_tag)::value;
         launch_key_gw<C, V>(GW, grid, stream, (const half_t*)Q, (const half_t*)K, (const half_t*)Vt,
                             (const half_t*)dO, L, D, (half_t*)dS, dK, dVt, sh.seqlens, c, s, sh.T, sh.heads,
-                            sh.kv_heads, nkt, BKV, sh.block_order, tph, sh.v_rows, kproj, vproj);
+                            sh.kv_heads, nkt, BKV, sh.block_order, ch, sh.v_rows, kproj, vproj);
     };
     using T_ = std::true_type;
     using F_ = std::false_type;
@@ -885,6 +915,13 @@ hipError_t launch_key_pass_to(const Shape& sh, const void* Q, const void* K, con
         if (sh.seqlens) go(F_{}, T_{}); else go(F_{}, F_{});
     }
     return hipGetLastError();
+}
+
+hipError_t launch_key_pass_to(const Shape& sh, const void* Q, const void* K, const void* Vt, const void* dO,
+                              const float* L, const float* D, void* dS, float c, float s, float* dK, float* dVt,
+                              const ProjectionOut& kproj, const ProjectionOut& vproj, hipStream_t stream) {
+    return launch_key_pass_chunk(sh, whole_problem(sh), Q, K, Vt, dO, L, D, dS, c, s, dK, dVt, kproj, vproj,
+                                 stream);
 }
 
 hipError_t launch_key_pass(const Shape& sh, const void* Q, const void* K, const void* Vt, const void* dO,
@@ -901,14 +938,17 @@ hipError_t launch_key_pass_projection(const Shape& sh, const void* Q, const void
 }
 
 template <int MODE>
-hipError_t launch_dq(const Shape& sh, const void* K, const void* dS, float s, float* dQ, const DqEpilogue& rot,
-                     hipStream_t stream) {
-    const int n_qblk = (sh.T + kDqRows - 1) / kDqRows, BH = sh.batch * sh.heads;
-    dim3 grid((unsigned)dq_pass_blocks(sh)), block(kDqThreads);
-    const long long tph = (long long)ds_tiles_per_head(sh);
+hipError_t launch_dq_chunk(const Shape& sh, const Chunk& ch, const void* K, const void* dS, float s, float* dQ,
+                           const DqEpilogue& rot, hipStream_t stream) {
+    // The chunk's 128-row query blocks: q_lo is even, q_hi is even or the last tile.
+    const int blk_lo = ch.q_lo / 2, blk_hi = (ch.q_hi + 1) / 2;
+    const int n_qblk = blk_hi - blk_lo, BH = sh.batch * sh.heads;
+    if (n_qblk <= 0) return hipSuccess;
+    const size_t per_unit = sh.block_order == 0 ? (size_t)(n_qblk + 1) / 2 : (size_t)n_qblk;
+    dim3 grid((unsigned)((size_t)BH * per_unit)), block(kDqThreads);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, stream, (const half_t*)K, (const half_t*)dS, dQ, sh.seqlens, s,
-                           sh.T, sh.heads, sh.kv_heads, n_qblk, BH, sh.block_order, tph, rot);
+                           sh.T, sh.heads, sh.kv_heads, n_qblk, BH, sh.block_order, ch, rot);
     };
     if (sh.causal) {
         if (sh.seqlens) go(sa_dq_kernel<true, true, MODE>); else go(sa_dq_kernel<true, false, MODE>);
@@ -916,6 +956,46 @@ hipError_t launch_dq(const Shape& sh, const void* K, const void* dS, float s, fl
         if (sh.seqlens) go(sa_dq_kernel<false, true, MODE>); else go(sa_dq_kernel<false, false, MODE>);
     }
     return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_dq(const Shape& sh, const void* K, const void* dS, float s, float* dQ, const DqEpilogue& rot,
+                     hipStream_t stream) {
+    return launch_dq_chunk<MODE>(sh, whole_problem(sh), K, dS, s, dQ, rot, stream);
+}
+
+size_t min_chunk_bytes(const Shape& sh) {
+    // The largest single 128-row block's dS.
+    const int nt = sh.T / kTile;
+    size_t most = 0;
+    for (int q = 0; q < nt; q += 2) most = std::max(most, chunk_bytes(sh, q, std::min(q + 2, nt)));
+    return most;
+}
+
+hipError_t launch_key_dq_chunked(const Shape& sh, const void* Q, const void* K, const void* Vt, const void* dO,
+                                 const float* L, const float* D, void* ws, size_t ws_bytes, float c, float s,
+                                 float* dQ, float* dK, float* dVt, hipStream_t stream) {
+    if (ws_bytes < min_chunk_bytes(sh)) return hipErrorInvalidValue;
+    const ProjectionOut none{nullptr, nullptr, 0};
+    const DqEpilogue plain{nullptr, nullptr, nullptr, nullptr, 0};
+    // Chunks from the last rows down: each takes as many 128-row blocks as
+    // fit in the workspace.  Causal, the first chunk reaches every key tile,
+    // so every later one accumulates onto finished or started sums.
+    const int nt = sh.T / kTile;
+    int q_hi = nt;
+    bool first = true;
+    while (q_hi > 0) {
+        int q_lo = ((q_hi - 1) / 2) * 2;               // one block at least (fits: checked above)
+        while (q_lo >= 2 && chunk_bytes(sh, q_lo - 2, q_hi) <= ws_bytes) q_lo -= 2;
+        const Chunk ch{q_lo, q_hi, ds_row_start(sh, q_lo), ds_row_start(sh, q_hi) - ds_row_start(sh, q_lo),
+                       first ? 0 : 1};
+        hipError_t e = launch_key_pass_chunk(sh, ch, Q, K, Vt, dO, L, D, ws, c, s, dK, dVt, none, none, stream);
+        if (e != hipSuccess) return e;
+        if ((e = launch_dq_chunk<kDqPlain>(sh, ch, K, ws, s, dQ, plain, stream)) != hipSuccess) return e;
+        first = false;
+        q_hi = q_lo;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_dq_pass(const Shape& sh, const void* K, const void* dS, float s, float* dQ,

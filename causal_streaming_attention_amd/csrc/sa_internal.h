@@ -22,6 +22,30 @@ inline size_t ds_tiles_per_head(const Shape& sh) {
     return sh.causal ? nt * (nt + 1) / 2 : nt * nt;
 }
 constexpr size_t kDsTileBytes = 64 * 64 * 2;
+// Per-head index of the first dS tile of query tile row q (rows below q hold
+// this many tiles).
+inline long long ds_row_start(const Shape& sh, int q) {
+    const long long nt = sh.T / 64;
+    return sh.causal ? (long long)q * (q + 1) / 2 : (long long)q * nt;
+}
+
+// A query-row chunk of the split backward: the 64-row query tiles
+// [q_lo, q_hi) (q_lo even, so that the dQ pass's 128-row blocks do not
+// straddle chunks).  Their dS tiles sit in the workspace at per-head index
+// (tile index - tile0), tph tiles per head.  accumulate: the key pass adds its
+// dK and dV to what the outputs already hold (every chunk after the first).
+struct Chunk {
+    int q_lo, q_hi;
+    long long tile0, tph;
+    int accumulate;
+};
+inline Chunk whole_problem(const Shape& sh) {
+    return Chunk{0, sh.T / 64, 0, (long long)ds_tiles_per_head(sh), 0};
+}
+// dS bytes a chunk needs.
+inline size_t chunk_bytes(const Shape& sh, int q_lo, int q_hi) {
+    return (size_t)sh.batch * sh.heads * (size_t)(ds_row_start(sh, q_hi) - ds_row_start(sh, q_lo)) * kDsTileBytes;
+}
 
 hipError_t launch_forward(const Shape& sh, const void* Q, const void* K, const void* Vt, void* O, float* L,
                           float c, hipStream_t stream);
@@ -31,6 +55,17 @@ hipError_t launch_key_pass(const Shape& sh, const void* Q, const void* K, const 
                            hipStream_t stream);
 hipError_t launch_dq_pass(const Shape& sh, const void* K, const void* dS, float s, float* dQ,
                           hipStream_t stream);
+// The split backward's key and dQ passes in query-row chunks over a dS
+// workspace of ws_bytes (which may be far smaller than the whole problem's):
+// chunks from the last rows to the first, each its key pass (dK and dV
+// accumulated across chunks in that fixed order) then its dQ pass.  The row
+// terms are not included.  Returns hipErrorInvalidValue, before launching
+// anything, if a single 128-row chunk does not fit.
+hipError_t launch_key_dq_chunked(const Shape& sh, const void* Q, const void* K, const void* Vt, const void* dO,
+                                 const float* L, const float* D, void* ws, size_t ws_bytes, float c, float s,
+                                 float* dQ, float* dK, float* dVt, hipStream_t stream);
+// The smallest workspace launch_key_dq_chunked accepts for the shape.
+size_t min_chunk_bytes(const Shape& sh);
 // The dQ pass with the rotated epilogue: dQ turned back by the inverse
 // half-split rotation (tables cos_t, sin_t fp32 [T][32]) and stored as the
 // bfloat16 Q slice of the token-major projection gradient dqkv [B][T][width].

@@ -1,8 +1,8 @@
 // sa_static.hip -- the split backward with its dS workspace in a static
 // device array owned by the library, for callers that cannot allocate
 // (code under HIP graph capture, tight serving loops, harnesses that forbid
-// hipMalloc).  The kernels are the split backward's own; only the workspace
-// differs.
+// hipMalloc).  The kernels are the chunked split backward's own (as many
+// query rows per chunk as the array holds); only the workspace differs.
 //
 // The array lives for the whole process on every GPU the library runs on
 // (each GPU holds its own copy at its own address).  In host code its name is
@@ -58,8 +58,7 @@ extern "C" sa_status sa_backward_static(const sa_shape* shape, const void* dO, c
     for (const void* p : ptrs)
         if (!aligned16(p)) return SA_ERR_ALIGN;
     if (!(std::isfinite(c) && c > 0.0f) || !(std::isfinite(s) && s > 0.0f)) return SA_ERR_ARGUMENT;
-    const size_t need = sa_backward_workspace_bytes(shape);
-    if (need > (size_t)SA_STATIC_SCRATCH_BYTES) return SA_ERR_TOO_LARGE;
+    if (sa_backward_chunked_min_bytes(shape) > (size_t)SA_STATIC_SCRATCH_BYTES) return SA_ERR_TOO_LARGE;
     void* ws = scratch_on_current_device();
     if (!ws) return SA_ERR_DEVICE;
     sa::Shape sh;
@@ -73,7 +72,8 @@ extern "C" sa_status sa_backward_static(const sa_shape* shape, const void* dO, c
     sh.v_rows = shape->v_rows;
     hipStream_t strm = (hipStream_t)stream;
     if (sa::launch_row_terms(sh, dO, O, D, strm) != hipSuccess) return SA_ERR_DEVICE;
-    if (sa::launch_key_pass(sh, Q, K, Vt, dO, L, D, ws, c, s, dK, dVt, strm) != hipSuccess) return SA_ERR_DEVICE;
-    if (sa::launch_dq_pass(sh, K, ws, s, dQ, strm) != hipSuccess) return SA_ERR_DEVICE;
+    if (sa::launch_key_dq_chunked(sh, Q, K, Vt, dO, L, D, ws, SA_STATIC_SCRATCH_BYTES, c, s, dQ, dK, dVt, strm) !=
+        hipSuccess)
+        return SA_ERR_DEVICE;
     return SA_OK;
 }

@@ -71,7 +71,8 @@ typedef enum sa_status {
     SA_ERR_WORKSPACE = 4,  /* dS_bytes < sa_backward_workspace_bytes(shape) */
     SA_ERR_ARGUMENT = 5,   /* c or s not finite and positive */
     SA_ERR_DEVICE = 6,     /* a HIP launch failed (read, and so cleared, by hipGetLastError) */
-    SA_ERR_TOO_LARGE = 7   /* sa_backward_static: the shape's dS workspace exceeds
+    SA_ERR_TOO_LARGE = 7   /* sa_backward_static: one 128-row block's dS
+                              (sa_backward_chunked_min_bytes) exceeds
                               SA_STATIC_SCRATCH_BYTES */
 } sa_status;
 
@@ -156,6 +157,35 @@ sa_status sa_backward_ex(const sa_shape* shape, const void* dO, const void* O, c
                          float* D, void* dS, size_t dS_bytes,
                          const void* Q, const void* K, const void* Vt, float c, float s,
                          float* dQ, float* dK, float* dVt, void* stream);
+
+/*
+ * The split backward over a dS workspace smaller than the whole problem's
+ * (StreamingAttentionSM86 page, banner "The query pass split in two around
+ * the key pass": the key pass stores dS, the dQ pass reads it back; here the
+ * query rows are taken in chunks so that one chunk's dS at a time occupies
+ * the workspace, which a small enough workspace keeps in the chip's last-level
+ * cache).  After the row terms, for each chunk of query rows from the last
+ * rows to the first: the key pass over that chunk's rows (dK and dV summed
+ * onto the earlier chunks' in that fixed order), then the dQ pass over the
+ * chunk's rows.  Each chunk is as many 128-row blocks as fit in dS_bytes.
+ *   Arguments: as sa_backward_ex.  dS_bytes may be anything from
+ *   sa_backward_chunked_min_bytes(shape) (one 128-row block's dS) up; with
+ *   dS_bytes >= sa_backward_workspace_bytes(shape) it is one chunk and the
+ *   results are bitwise sa_backward_ex's.
+ *   Results: deterministic for equal inputs, shape, block order and
+ *   dS_bytes; dK and dV sum the chunks in a different order than the
+ *   one-chunk backward, so they may differ from it in rounding.
+ *   Errors: SA_ERR_WORKSPACE if dS_bytes < sa_backward_chunked_min_bytes;
+ *   otherwise as sa_backward_ex.
+ */
+sa_status sa_backward_chunked(const sa_shape* shape, const void* dO, const void* O, const float* L,
+                              float* D, void* dS, size_t dS_bytes,
+                              const void* Q, const void* K, const void* Vt, float c, float s,
+                              float* dQ, float* dK, float* dVt, void* stream);
+
+/* The smallest dS_bytes sa_backward_chunked accepts (the largest single
+ * 128-row block's dS); 0 if the shape fails admission. */
+size_t sa_backward_chunked_min_bytes(const sa_shape* shape);
 
 /*
  * The backward's three launches, one at a time, for measurement and tests.
@@ -279,16 +309,19 @@ sa_status sa_backward_two_pass_projection(const sa_shape* shape, const void* dO,
 /*
  * The split backward without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
- * harnesses that forbid hipMalloc): sa_backward_ex's three launches with the
- * dS workspace in a static device array of SA_STATIC_SCRATCH_BYTES that the
+ * harnesses that forbid hipMalloc): sa_backward_chunked with the dS
+ * workspace in a static device array of SA_STATIC_SCRATCH_BYTES that the
  * library holds on each GPU until the process ends.  The call itself
  * allocates nothing.
  *   Arguments: as sa_backward_ex without dS and dS_bytes.
- *   Limit: a shape whose sa_backward_workspace_bytes exceeds
+ *   Limit: a shape whose sa_backward_chunked_min_bytes exceeds
  *          SA_STATIC_SCRATCH_BYTES returns SA_ERR_TOO_LARGE (checked before
- *          anything else touches the GPU), e.g. batch 1, T = 1024, 8 heads
- *          needs 8.9 MB; T = 4096, 32 heads needs 545 MB and is refused.
- *   Results: bitwise equal to sa_backward_ex's for the same inputs.
+ *          anything else touches the GPU): e.g. batch 1, 32 heads, causal,
+ *          runs up to T = 8192 (T = 16384 needs 134 MB for one 128-row
+ *          block).
+ *   Results: sa_backward_chunked's with dS_bytes = SA_STATIC_SCRATCH_BYTES:
+ *          bitwise sa_backward_ex's when the whole dS fits (e.g. batch 1,
+ *          T = 1024, 8 heads: 8.9 MB), within rounding of it otherwise.
  *   Concurrency: every call on one GPU shares that GPU's array; calls that
  *          overlap on one GPU (other streams, other host threads) race.  Calls
  *          on one stream run in order and are safe.

@@ -267,9 +267,11 @@ def test_a_library_built_from_other_sources_is_refused(monkeypatch):
 
 def test_static_scratch_backward_rejects_before_touching_the_gpu(lib):
     """sa_backward_static checks shape, pointers, scales and its size limit before any HIP call."""
+    fits = shape(batch=1, T=8192, heads=32, kv=8)
+    assert sa.sa_backward_chunked_min_bytes(fits) <= sa.SA_STATIC_SCRATCH_BYTES
     P = 256
-    big = shape(batch=1, T=4096, heads=32, kv=8)
-    assert sa.sa_backward_workspace_bytes(big) > sa.SA_STATIC_SCRATCH_BYTES
+    big = shape(batch=1, T=16384, heads=32, kv=8)          # one 128-row block alone needs 134 MB of dS
+    assert sa.sa_backward_chunked_min_bytes(big) > sa.SA_STATIC_SCRATCH_BYTES
     args = [P] * 7 + [sa.base2_scale(0.125), 0.125] + [P] * 3 + [None]
     f = lib.sa_backward_static
     assert f(ctypes.byref(big), *args) == sa.SA_ERR_TOO_LARGE
@@ -283,3 +285,20 @@ def test_static_scratch_backward_rejects_before_touching_the_gpu(lib):
     bad[7] = float("nan")
     assert f(ctypes.byref(shape()), *bad) == sa.SA_ERR_ARGUMENT
     assert "static scratch" in sa.sa_status_string(sa.SA_ERR_TOO_LARGE)
+
+
+def test_chunked_backward_minimum_workspace(lib):
+    """The chunked backward needs one 128-row block's dS at least: the block with the most tiles."""
+    tile = 64 * 64 * 2
+    # causal T = 320 (5 tiles): blocks hold rows {0,1}, {2,3}, {4}: 1+2, 3+4, 5 tiles; the most is 7
+    assert sa.sa_backward_chunked_min_bytes(shape(batch=2, T=320, heads=4, kv=2)) == 2 * 4 * 7 * tile
+    # full square T = 320: two rows of 5 tiles
+    assert sa.sa_backward_chunked_min_bytes(shape(batch=1, T=320, heads=2, kv=2, causal=0)) == 2 * 10 * tile
+    assert sa.sa_backward_chunked_min_bytes(shape(T=100)) == 0
+    P = 256
+    sh = shape(batch=1, T=256, heads=2, kv=1)
+    need = sa.sa_backward_chunked_min_bytes(sh)
+    args = [P] * 5 + [need - 16] + [P] * 3 + [sa.base2_scale(0.125), 0.125] + [P] * 3 + [None]
+    assert lib.sa_backward_chunked(ctypes.byref(sh), *args) == sa.SA_ERR_WORKSPACE
+    args[4] = None
+    assert lib.sa_backward_chunked(ctypes.byref(sh), *args) == sa.SA_ERR_NULL

@@ -1,20 +1,23 @@
 """The backward that allocates nothing (sa_backward_static): its dS workspace is
-the library's static device array.  Called through the C ABI on two problems in
-a row, the second smaller, it must give exactly the bits of sa_backward_ex with a
-caller-provided workspace (the same kernels), and the smaller one also matches
-the oracle.  Needs an MI355X."""
+the library's static device array, taken in query-row chunks when the problem's
+dS is larger.  Called through the C ABI on three problems in a row, each smaller
+than the one before: the benchmark's workload (545 MB of dS, chunked) matches
+sa_backward_ex (D and dQ bitwise, dK and dV within rounding); the two that fit
+whole give exactly sa_backward_ex's bits, and the smallest also matches the
+oracle.  Needs an MI355X."""
 import numpy as np
 import pytest
 import torch
 
 import causal_streaming_attention_amd as sa
 from causal_streaming_attention_amd.workloads import SCALE, make_inputs
-from parity_util import C, check_forward, check_grad, full_reference, run_gpu, say
+from parity_util import C, check_forward, check_grad, full_reference, rel_l2, run_gpu, say
 
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # B, T, H, KV, causal, seqlens: the first needs 34.6 MB of dS, the second 0.8 MB
+    # B, T, H, KV, causal, seqlens: 545 MB of dS (chunked), then 34.6 MB, then 0.8 MB
+    (1, 4096, 32, 8, True, None),
     (1, 2048, 8, 2, True, None),
     (3, 256, 4, 2, False, [256, 77, 0]),
 ]
@@ -37,11 +40,17 @@ def test_static_scratch_backward_two_calls_in_a_row():
         say(f"case static-scratch backward call {i}: B={B} T={T} H={H} KV={KV} causal={causal}")
         x = make_inputs(B, T, H, KV, seed=700 + i, seqlens=seqlens)
         buf, want = run_gpu(x, causal)          # forward + sa_backward_ex with its own workspace
-        assert buf.ws_bytes <= sa.SA_STATIC_SCRATCH_BYTES
         got = _static_backward(buf)
-        for k in ("D", "dQ", "dK", "dVt"):
-            assert np.array_equal(got[k], want[k]), f"call {i}: {k} differs from sa_backward_ex"
-        if i == 1:
+        if buf.ws_bytes > sa.SA_STATIC_SCRATCH_BYTES:
+            for k in ("D", "dQ"):
+                assert np.array_equal(got[k], want[k]), f"call {i}: {k} differs from sa_backward_ex"
+            for k in ("dK", "dVt"):
+                e = rel_l2(got[k], want[k])
+                assert e <= 1e-5, f"call {i}: {k} rel L2 {e:.2e} from sa_backward_ex"
+        else:
+            for k in ("D", "dQ", "dK", "dVt"):
+                assert np.array_equal(got[k], want[k]), f"call {i}: {k} differs from sa_backward_ex"
+        if i == len(CASES) - 1:
             ref = full_reference(x, causal)
             check_forward(want["O"], want["L"], ref["O"], ref["L"], "static scratch")
             for k in ("dQ", "dK", "dVt"):
@@ -49,11 +58,12 @@ def test_static_scratch_backward_two_calls_in_a_row():
 
 
 def test_static_scratch_refuses_a_problem_beyond_its_size():
-    """T = 4096 with 32 heads needs 545 MB of dS: refused before any launch, outputs untouched."""
+    """T = 16384 with 32 heads needs 134 MB of dS for a single 128-row block: refused before any launch,
+    outputs untouched."""
     say("case static-scratch too large")
-    T, H, KV = 4096, 32, 8
+    T, H, KV = 16384, 32, 8
     shape = sa.make_shape(1, T, H, KV, True)
-    assert sa.sa_backward_workspace_bytes(shape) > sa.SA_STATIC_SCRATCH_BYTES
+    assert sa.sa_backward_chunked_min_bytes(shape) > sa.SA_STATIC_SCRATCH_BYTES
     f16, f32 = torch.float16, torch.float32
     t = lambda *s, d=f16: torch.zeros(*s, dtype=d, device="cuda")
     dQ = torch.full((1, H, T, 64), 5.0, dtype=f32, device="cuda")
