@@ -964,13 +964,7 @@ hipError_t launch_dq(const Shape& sh, const void* K, const void* dS, float s, fl
     return launch_dq_chunk<MODE>(sh, whole_problem(sh), K, dS, s, dQ, rot, stream);
 }
 
-size_t min_chunk_bytes(const Shape& sh) {
-    // The largest single 128-row block's dS.
-    const int nt = sh.T / kTile;
-    size_t most = 0;
-    for (int q = 0; q < nt; q += 2) most = std::max(most, chunk_bytes(sh, q, std::min(q + 2, nt)));
-    return most;
-}
+size_t min_chunk_bytes(const Shape& sh) { return largest_block_bytes(sh); }
 
 hipError_t launch_key_dq_chunked(const Shape& sh, const void* Q, const void* K, const void* Vt, const void* dO,
                                  const float* L, const float* D, void* ws, size_t ws_bytes, float c, float s,
@@ -981,14 +975,11 @@ hipError_t launch_key_dq_chunked(const Shape& sh, const void* Q, const void* K, 
     // Chunks from the last rows down: each takes as many 128-row blocks as
     // fit in the workspace.  Causal, the first chunk reaches every key tile,
     // so every later one accumulates onto finished or started sums.
-    const int nt = sh.T / kTile;
-    int q_hi = nt;
+    int q_hi = sh.T / kTile;
     bool first = true;
     while (q_hi > 0) {
-        int q_lo = ((q_hi - 1) / 2) * 2;               // one block at least (fits: checked above)
-        while (q_lo >= 2 && chunk_bytes(sh, q_lo - 2, q_hi) <= ws_bytes) q_lo -= 2;
-        const Chunk ch{q_lo, q_hi, ds_row_start(sh, q_lo), ds_row_start(sh, q_hi) - ds_row_start(sh, q_lo),
-                       first ? 0 : 1};
+        const Chunk ch = next_chunk(sh, q_hi, ws_bytes, first);
+        const int q_lo = ch.q_lo;
         hipError_t e = launch_key_pass_chunk(sh, ch, Q, K, Vt, dO, L, D, ws, c, s, dK, dVt, none, none, stream);
         if (e != hipSuccess) return e;
         if ((e = launch_dq_chunk<kDqPlain>(sh, ch, K, ws, s, dQ, plain, stream)) != hipSuccess) return e;

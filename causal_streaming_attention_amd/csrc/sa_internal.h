@@ -46,6 +46,27 @@ inline Chunk whole_problem(const Shape& sh) {
 inline size_t chunk_bytes(const Shape& sh, int q_lo, int q_hi) {
     return (size_t)sh.batch * sh.heads * (size_t)(ds_row_start(sh, q_hi) - ds_row_start(sh, q_lo)) * kDsTileBytes;
 }
+// The largest single 128-row block's dS: the least workspace a chunked
+// backward can run in.
+inline size_t largest_block_bytes(const Shape& sh) {
+    const int nt = sh.T / 64;
+    size_t most = 0;
+    for (int q = 0; q < nt; q += 2) {
+        const size_t b = chunk_bytes(sh, q, q + 2 < nt ? q + 2 : nt);
+        if (b > most) most = b;
+    }
+    return most;
+}
+// The next chunk below query tile q_hi (> 0): as many 128-row blocks,
+// downwards from q_hi, as fit in ws_bytes (at least one; the caller checks
+// ws_bytes >= largest_block_bytes).  Chunks taken from the last rows to the
+// first: the first one reaches every key tile, every later one accumulates.
+inline Chunk next_chunk(const Shape& sh, int q_hi, size_t ws_bytes, bool first) {
+    int q_lo = ((q_hi - 1) / 2) * 2;
+    while (q_lo >= 2 && chunk_bytes(sh, q_lo - 2, q_hi) <= ws_bytes) q_lo -= 2;
+    return Chunk{q_lo, q_hi, ds_row_start(sh, q_lo), ds_row_start(sh, q_hi) - ds_row_start(sh, q_lo),
+                 first ? 0 : 1};
+}
 
 hipError_t launch_forward(const Shape& sh, const void* Q, const void* K, const void* Vt, void* O, float* L,
                           float c, hipStream_t stream);
