@@ -139,12 +139,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void dma16(const void* g, char* lds_wave_base) {
     __builtin_amdgcn_global_load_lds(g, (lds_void*)((__attribute__((address_space(3))) char*)lds_wave_base), 16, 0, 0);
 }
-// 16-byte buffer load at voffset + OFF within the resource into LDS at
-// lds_wave_base + OFF + 16 lane (the offset field moves both addresses).
+// 16-byte buffer load at soffset + voffset + OFF within the resource into
+// LDS at lds_wave_base + OFF + 16 lane (the offset field moves both
+// addresses; the scalar offset only the memory address).
 template <int OFF>
-__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voffset, char* lds_wave_base) {
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t soffset,
+                                          char* lds_wave_base) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)((__attribute__((address_space(3))) char*)lds_wave_base),
-                                             16, voffset, 0, OFF, 0);
+                                             16, voffset, soffset, OFF, 0);
 }
 __device__ __forceinline__ void dma4_buf(__amdgpu_buffer_rsrc_t r, uint32_t voffset, char* lds_wave_base) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)((__attribute__((address_space(3))) char*)lds_wave_base),
@@ -236,30 +238,49 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     const uint32_t dma_off1 = (uint32_t)(dma_row * kHeadDim + ((lane & 7) ^ swz_key(dma_row + 8)) * 8) * 2u;
     // The item's rows as buffer resources built on the scalar unit: the loads
     // take fixed per-lane offsets, so no vector instruction forms an address.
-    // L's and D's resources hold the item's 32 values each; the other 32 lanes
-    // of their 64-lane loads fall outside and fill unused slots with zeros.
+    // Q and dO: one resource per head over its T rows (rebuilt only when the
+    // walk moves on to the slot's next head), the sub-tile a scalar offset of
+    // sub x 4 KB; the record count bounds the per-lane offsets to the head.
+    // L's and D's resources hold the item's 32 values each; the other 32
+    // lanes of their 64-lane loads fall outside and fill unused slots with
+    // zeros.
     const uint32_t ld_off_l = 4u * (uint32_t)lane, ld_off_d = 4u * (uint32_t)lane - 128u;
+    auto rows_rsrc = [&](const half_t* p, int hd) {
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(p + ((size_t)b * H + hd) * T * kHeadDim), (short)0,
+                                                 T * kHeadDim * 2, kBufferRsrcWord3);
+    };
+    int dma_head = kv * G + slot;
+    __amdgpu_buffer_rsrc_t q_head = rows_rsrc(Q, dma_head), o_head = rows_rsrc(dO, dma_head);
+    const float* l_head = L + ((size_t)b * H + dma_head) * T;
+    const float* d_head = D + ((size_t)b * H + dma_head) * T;
     auto issue_item = [&](int head, int sub, int buf) {
-        const size_t rowbase = ((size_t)b * H + head) * T + (size_t)sub * kSubRows;
-        const __amdgpu_buffer_rsrc_t qr =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(Q + rowbase * kHeadDim), (short)0, kSubBytes, kBufferRsrcWord3);
-        const __amdgpu_buffer_rsrc_t orr =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(dO + rowbase * kHeadDim), (short)0, kSubBytes, kBufferRsrcWord3);
+        if (head != dma_head) {
+            dma_head = head;
+            q_head = rows_rsrc(Q, head);
+            o_head = rows_rsrc(dO, head);
+            l_head = L + ((size_t)b * H + head) * T;
+            d_head = D + ((size_t)b * H + head) * T;
+        }
+        const uint32_t so = (uint32_t)sub * (uint32_t)kSubBytes;
         char* base = wstage + buf * kItemBytes;
-        dma16_buf<0>(qr, dma_off0, base);
-        dma16_buf<1024>(qr, dma_off1, base);
-        dma16_buf<2048>(qr, dma_off0, base);
-        dma16_buf<3072>(qr, dma_off1, base);
-        dma16_buf<0>(orr, dma_off0, base + kSubBytes);
-        dma16_buf<1024>(orr, dma_off1, base + kSubBytes);
-        dma16_buf<2048>(orr, dma_off0, base + kSubBytes);
-        dma16_buf<3072>(orr, dma_off1, base + kSubBytes);
-        dma4_buf(__builtin_amdgcn_make_buffer_rsrc((void*)(L + rowbase), (short)0, kSubRows * 4, kBufferRsrcWord3),
+        dma16_buf<0>(q_head, dma_off0, so, base);
+        dma16_buf<1024>(q_head, dma_off1, so, base);
+        dma16_buf<2048>(q_head, dma_off0, so, base);
+        dma16_buf<3072>(q_head, dma_off1, so, base);
+        dma16_buf<0>(o_head, dma_off0, so, base + kSubBytes);
+        dma16_buf<1024>(o_head, dma_off1, so, base + kSubBytes);
+        dma16_buf<2048>(o_head, dma_off0, so, base + kSubBytes);
+        dma16_buf<3072>(o_head, dma_off1, so, base + kSubBytes);
+        const int r = sub * kSubRows;
+        dma4_buf(__builtin_amdgcn_make_buffer_rsrc((void*)(l_head + r), (short)0, kSubRows * 4, kBufferRsrcWord3),
                  ld_off_l, base + 2 * kSubBytes);
-        dma4_buf(__builtin_amdgcn_make_buffer_rsrc((void*)(D + rowbase), (short)0, kSubRows * 4, kBufferRsrcWord3),
+        dma4_buf(__builtin_amdgcn_make_buffer_rsrc((void*)(d_head + r), (short)0, kSubRows * 4, kBufferRsrcWord3),
                  ld_off_d, base + 2 * kSubBytes + 256);
     };
 
+    // The dS store's per-head base, rebuilt when the walk reaches the slot's next head.
+    int ds_head_id = -1;
+    half_t* ds_head = dS;
     // Items in order: for each of the slot's heads, sub-tiles from the last down.
     int head = kv * G + slot, sub = sub_hi - 1;
     if (n_items > 0) issue_item(head, sub, 0);
@@ -422,11 +443,15 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
         // once; streamed past L2 it neither evicts the Q/dO rows the walk
         // reuses nor stalls the walk behind L2 write-backs.
         if (store_ds) {
-            const int qt = sub >> 1;
-            const size_t tile = (CAUSAL ? (size_t)qt * (qt + 1) / 2 + kt : (size_t)qt * (T / kTile) + kt) -
-                                (size_t)ch.tile0;
-            half_t* dsp = dS + (((size_t)b * H + head) * (size_t)ch.tph + tile) * (kTile * kTile) +
-                          (size_t)(2 * (sub & 1) + khalf) * 1024 + 8 * lane;
+            if (head != ds_head_id) {
+                ds_head_id = head;
+                ds_head = dS + ((size_t)b * H + head) * (size_t)ch.tph * (kTile * kTile);
+            }
+            // Tile indices stay below 2^31 (T <= 2^20: at most 2^27 tiles per head).
+            const uint32_t qt = (uint32_t)sub >> 1;
+            const uint32_t tile = (CAUSAL ? (qt * (qt + 1)) >> 1 : qt * (uint32_t)(T / kTile)) + (uint32_t)kt -
+                                  (uint32_t)ch.tile0;
+            half_t* dsp = ds_head + (size_t)tile * (kTile * kTile) + (2 * (sub & 1) + khalf) * 1024 + 8 * lane;
             __builtin_nontemporal_store(half8_from_words(wd[0], wd[1], wd[2], wd[3]), (half8*)dsp);
             __builtin_nontemporal_store(half8_from_words(wd[4], wd[5], wd[6], wd[7]), (half8*)(dsp + 512));
         }
@@ -590,12 +615,16 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
     // when the backward is not chunked).
     const int blk_lo = ch.q_lo / 2;
     int bh, n_items, items[2];
-    if (block_order == 0) {
+    if (block_order == kOrderPairs) {
         int pair;
         pair_schedule((int)blockIdx.x, (BH / H) * KV, H / KV, pair, bh);
         items[0] = blk_lo + n_qblk - 1 - pair;
         items[1] = blk_lo + pair;
         n_items = pair < n_qblk - 1 - pair ? 2 : 1;
+    } else if (block_order == kOrderSingle) {  // one block of rows per block, the longest first
+        items[0] = items[1] = blk_lo + n_qblk - 1 - (int)(blockIdx.x / BH);
+        bh = (int)(blockIdx.x % BH);
+        n_items = 1;
     } else {
         items[0] = items[1] = blk_lo + (int)(blockIdx.x % n_qblk);
         bh = (int)(blockIdx.x / n_qblk);
@@ -870,8 +899,9 @@ size_t row_terms_blocks(const Shape& sh) {
 }
 size_t key_pass_blocks(const Shape& sh) { return (size_t)sh.batch * sh.kv_heads * (sh.T / kTile); }
 size_t dq_pass_blocks(const Shape& sh) {
-    const size_t n_qblk = (size_t)((sh.T + kDqRows - 1) / kDqRows);
-    return (size_t)sh.batch * sh.heads * (sh.block_order == 0 ? (n_qblk + 1) / 2 : n_qblk);
+    const size_t units = (size_t)sh.batch * sh.heads;
+    const int n_qblk = (sh.T + kDqRows - 1) / kDqRows;
+    return tile_schedule_blocks(tile_schedule(sh, units, n_qblk), units, n_qblk);
 }
 
 hipError_t launch_row_terms(const Shape& sh, const void* dO, const void* O, float* D, hipStream_t stream) {
@@ -944,11 +974,11 @@ hipError_t launch_dq_chunk(const Shape& sh, const Chunk& ch, const void* K, cons
     const int blk_lo = ch.q_lo / 2, blk_hi = (ch.q_hi + 1) / 2;
     const int n_qblk = blk_hi - blk_lo, BH = sh.batch * sh.heads;
     if (n_qblk <= 0) return hipSuccess;
-    const size_t per_unit = sh.block_order == 0 ? (size_t)(n_qblk + 1) / 2 : (size_t)n_qblk;
-    dim3 grid((unsigned)((size_t)BH * per_unit)), block(kDqThreads);
+    const int order = tile_schedule(sh, (size_t)BH, n_qblk);
+    dim3 grid((unsigned)tile_schedule_blocks(order, (size_t)BH, n_qblk)), block(kDqThreads);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, stream, (const half_t*)K, (const half_t*)dS, dQ, sh.seqlens, s,
-                           sh.T, sh.heads, sh.kv_heads, n_qblk, BH, sh.block_order, ch, rot);
+                           sh.T, sh.heads, sh.kv_heads, n_qblk, BH, order, ch, rot);
     };
     if (sh.causal) {
         if (sh.seqlens) go(sa_dq_kernel<true, true, MODE>); else go(sa_dq_kernel<true, false, MODE>);

@@ -110,12 +110,16 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
     // p, with the heads of one kv head kept on one XCD.  Order 1: one query
     // tile per block in plain order.
     int bh, n_items, items[2];
-    if (block_order == 0) {
+    if (block_order == kOrderPairs) {
         int pair;
         pair_schedule((int)blockIdx.x, (BH / H) * KV, H / KV, pair, bh);
         items[0] = n_qtiles - 1 - pair;
         items[1] = pair;
         n_items = pair < items[0] ? 2 : 1;
+    } else if (block_order == kOrderSingle) {  // one tile per block, the longest first
+        items[0] = items[1] = n_qtiles - 1 - (int)(blockIdx.x / BH);
+        bh = (int)(blockIdx.x % BH);
+        n_items = 1;
     } else {
         items[0] = items[1] = (int)(blockIdx.x % n_qtiles);
         bh = (int)(blockIdx.x / n_qtiles);
@@ -133,6 +137,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
     // Key tiles the block walks, and the keys each wave needs.
     int kend = CAUSAL ? min(q0 + kFwdRows, T) : T;
     if (VARLEN) kend = min(kend, len);
+    if (VARLEN && q0 >= len) kend = 0;  // every row is padding: no key tile to walk
     const int n_kt = (kend + kTile - 1) / kTile;
     int kend_w = CAUSAL ? qw + 32 : T;
     if (VARLEN) kend_w = min(kend_w, len);
@@ -446,9 +451,11 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
 
 }  // namespace
 
+int forward_order(const Shape& sh) {
+    return tile_schedule(sh, (size_t)sh.batch * sh.heads, (sh.T + kFwdRows - 1) / kFwdRows);
+}
 size_t forward_blocks(const Shape& sh) {
-    const size_t n_qtiles = (size_t)((sh.T + kFwdRows - 1) / kFwdRows);
-    return (sh.block_order == 0 ? (n_qtiles + 1) / 2 : n_qtiles) * sh.batch * sh.heads;
+    return tile_schedule_blocks(forward_order(sh), (size_t)sh.batch * sh.heads, (sh.T + kFwdRows - 1) / kFwdRows);
 }
 
 hipError_t launch_forward(const Shape& sh, const void* Q, const void* K, const void* Vt, void* O, float* L,
@@ -459,7 +466,7 @@ hipError_t launch_forward(const Shape& sh, const void* Q, const void* K, const v
     auto args = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, stream, (const half_t*)Q, (const half_t*)K, (const half_t*)Vt,
                            (half_t*)O, L, sh.seqlens, c, sh.T, sh.heads, sh.kv_heads, n_qtiles, BH,
-                           sh.block_order);
+                           forward_order(sh));
     };
     const bool varlen = sh.seqlens != nullptr;
     auto go = [&](auto rows_tag) {

@@ -14,6 +14,24 @@ struct Shape {
     int v_rows;  // 1: V and dV as rows [T][64] (like K), 0: V^T and dV^T
 };
 
+// Block schedules of the kernels whose blocks take query tiles (forward,
+// query pass, dQ pass).  Pairs: each block takes the tiles (n - 1 - p, p),
+// whose causal walks add up to the same length, so a grid of many rounds
+// drains evenly; single: one tile per block, the longest first, used when a
+// grid of single tiles fits the chip at once (two blocks on each of 256 CUs),
+// where pairing would only halve the blocks in flight; plain: one tile per
+// block in natural order (the caller's block_order = 1).  Every schedule
+// gives bitwise the same results.
+constexpr int kOrderPairs = 0, kOrderPlain = 1, kOrderSingle = 2;
+constexpr size_t kSingleTileGridMax = 512;
+inline int tile_schedule(const Shape& sh, size_t units, int n_tiles) {
+    if (sh.block_order == 1) return kOrderPlain;
+    return units * (size_t)n_tiles <= kSingleTileGridMax ? kOrderSingle : kOrderPairs;
+}
+inline size_t tile_schedule_blocks(int order, size_t units, int n_tiles) {
+    return units * (order == kOrderPairs ? (size_t)(n_tiles + 1) / 2 : (size_t)n_tiles);
+}
+
 // dS workspace geometry: one fp16 64x64 tile per (batch, query head, query
 // tile qt, key tile kt) that the dQ pass reads.  Causal: kt <= qt, tile index
 // qt (qt + 1) / 2 + kt; otherwise the full square, qt * nt + kt.

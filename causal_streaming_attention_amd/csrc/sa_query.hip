@@ -97,12 +97,16 @@ __global__ __launch_bounds__(kQpThreads, 2) void sa_query_kernel(
     // p) of equal causal length with the heads of one kv head on one XCD
     // (order 0), or one tile per block in plain order (order 1).
     int bh, n_items, items[2];
-    if (block_order == 0) {
+    if (block_order == kOrderPairs) {
         int pair;
         pair_schedule((int)blockIdx.x, (BH / H) * KV, H / KV, pair, bh);
         items[0] = n_qtiles - 1 - pair;
         items[1] = pair;
         n_items = pair < items[0] ? 2 : 1;
+    } else if (block_order == kOrderSingle) {  // one tile per block, the longest first
+        items[0] = items[1] = n_qtiles - 1 - (int)(blockIdx.x / BH);
+        bh = (int)(blockIdx.x % BH);
+        n_items = 1;
     } else {
         items[0] = items[1] = (int)(blockIdx.x % n_qtiles);
         bh = (int)(blockIdx.x / n_qtiles);
@@ -164,6 +168,7 @@ __global__ __launch_bounds__(kQpThreads, 2) void sa_query_kernel(
         const int row_limit = VARLEN ? len : T;
         int kend = CAUSAL ? min(q0 + kQpRows, T) : T;
         if (VARLEN) kend = min(kend, len);
+        if (VARLEN && q0 >= len) kend = 0;  // every row is padding: no key tile to walk
         const int n_kt = (kend + kTile - 1) / kTile;
         int kend_w = CAUSAL ? qw + 32 : T;
         if (VARLEN) kend_w = min(kend_w, len);
@@ -359,9 +364,11 @@ __global__ __launch_bounds__(kQpThreads, 2) void sa_query_kernel(
 
 }  // namespace
 
+int query_order(const Shape& sh) {
+    return tile_schedule(sh, (size_t)sh.batch * sh.heads, (sh.T + kQpRows - 1) / kQpRows);
+}
 size_t query_pass_blocks(const Shape& sh) {
-    const size_t n_qtiles = (size_t)((sh.T + kQpRows - 1) / kQpRows);
-    return (sh.block_order == 0 ? (n_qtiles + 1) / 2 : n_qtiles) * sh.batch * sh.heads;
+    return tile_schedule_blocks(query_order(sh), (size_t)sh.batch * sh.heads, (sh.T + kQpRows - 1) / kQpRows);
 }
 
 hipError_t launch_query_pass_to(const Shape& sh, const void* dO, const void* O, const float* L, const void* Q,
@@ -373,7 +380,7 @@ hipError_t launch_query_pass_to(const Shape& sh, const void* dO, const void* O, 
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, stream, (const half_t*)Q, (const half_t*)K, (const half_t*)Vt,
                            (const half_t*)dO, (const half_t*)O, L, D, dQ, sh.seqlens, c, s, sh.T, sh.heads,
-                           sh.kv_heads, n_qtiles, BH, sh.block_order, qproj);
+                           sh.kv_heads, n_qtiles, BH, query_order(sh), qproj);
     };
     const bool varlen = sh.seqlens != nullptr;
     auto pick = [&](auto rows_tag) {

@@ -206,6 +206,23 @@ def test_determinism_and_block_order():
         assert np.array_equal(a[k], c[k], equal_nan=True), f"{k} differs between block orders"
 
 
+@pytest.mark.parametrize("B,T,H,KV,causal,seqlens", [
+    (1, 1024, 8, 8, True, None),          # the T = 1024 workload's shape: one tile per block, longest first
+    (2, 320, 4, 2, True, [320, 77]),
+    (3, 256, 2, 2, False, [0, 200, 256]),
+])
+def test_block_orders_agree_bitwise_on_small_grids(B, T, H, KV, causal, seqlens):
+    """Grids small enough to fit the chip at once take one tile per block, longest first; the plain order
+    gives the same bits, for the split and the two-launch backward."""
+    say(f"case block orders B={B} T={T} H={H} KV={KV} causal={causal}")
+    x = make_inputs(B, T, H, KV, seed=40 + T, seqlens=seqlens)
+    for path in ("split", "two_pass"):
+        _, a = run_gpu(x, causal, block_order=0, path=path)
+        _, b = run_gpu(x, causal, block_order=1, path=path)
+        for k in a:
+            assert np.array_equal(a[k], b[k], equal_nan=True), f"{path}: {k} differs between block orders"
+
+
 def test_grouped_heads_equal_repeated_heads():
     say("case gqa-vs-mha")
     x = make_inputs(1, 256, 8, 2, seed=21)
