@@ -169,7 +169,14 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     const bool store_ds = dS != nullptr;
 
     int kt, bkv;
-    if (block_order == 0) {  // key tile 0 first: it walks every query
+    if (VARLEN && block_order == 0 && BKV / KV <= kMaxRankedBatch) {
+        // Variable lengths: the longest sequences' key tiles first (their
+        // walks are the longest), key tile 0 first within each.
+        const int per_b = KV * nkt;
+        const int r = (int)blockIdx.x / per_b, rest = (int)blockIdx.x % per_b;
+        kt = rest / KV;
+        bkv = batch_of_rank(seqlens, BKV / KV, T, r) * KV + rest % KV;
+    } else if (block_order == 0) {  // key tile 0 first: it walks every query
         kt = (int)(blockIdx.x / BKV);
         bkv = (int)(blockIdx.x % BKV);
     } else {
@@ -615,7 +622,16 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
     // when the backward is not chunked).
     const int blk_lo = ch.q_lo / 2;
     int bh, n_items, items[2];
-    if (block_order == kOrderPairs) {
+    if (VARLEN && block_order != kOrderPlain && BH / H <= kMaxRankedBatch) {
+        // Variable lengths: the longest sequences' blocks first, then the
+        // schedule's order within each sequence.
+        const int per_b = H * (block_order == kOrderPairs ? (n_qblk + 1) / 2 : n_qblk);
+        const int r = (int)blockIdx.x / per_b, rest = (int)blockIdx.x % per_b, k = rest / H;
+        bh = batch_of_rank(seqlens, BH / H, T, r) * H + rest % H;
+        items[0] = blk_lo + n_qblk - 1 - k;
+        items[1] = blk_lo + k;
+        n_items = (block_order == kOrderPairs && k < n_qblk - 1 - k) ? 2 : 1;
+    } else if (block_order == kOrderPairs) {
         int pair;
         pair_schedule((int)blockIdx.x, (BH / H) * KV, H / KV, pair, bh);
         items[0] = blk_lo + n_qblk - 1 - pair;

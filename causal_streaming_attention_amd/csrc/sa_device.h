@@ -85,6 +85,23 @@ __device__ __forceinline__ void pair_schedule(int block, int n_groups, int group
     }
 }
 
+// Variable-length batches of at most 64 sequences: the batch entry of rank r
+// when the entries are ordered by descending sequence length (ties by index),
+// so that block indices can hand out the longest sequences' work first.
+// Every lane of the wave returns the same value.
+constexpr int kMaxRankedBatch = 64;
+__device__ __forceinline__ int batch_of_rank(const int32_t* seqlens, int B, int T, int r) {
+    const int lane = threadIdx.x & 63;
+    const int mine = lane < B ? min(max(seqlens[lane], 0), T) : -1;
+    int rank = 0;
+    for (int j = 0; j < B; ++j) {
+        const int other = __builtin_amdgcn_readlane(mine, j);
+        rank += (other > mine || (other == mine && j < lane)) ? 1 : 0;
+    }
+    const unsigned long long hit = __builtin_amdgcn_ballot_w64(lane < B && rank == r);
+    return (int)__builtin_ctzll(hit);
+}
+
 // Word 3 of a raw buffer resource on gfx950 (32-bit data format, no swizzle,
 // no index stride): loads address base + voffset + soffset, bounded by the
 // record count in bytes.

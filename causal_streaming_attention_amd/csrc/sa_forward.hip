@@ -110,7 +110,16 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sa_forward_kernel(
     // p, with the heads of one kv head kept on one XCD.  Order 1: one query
     // tile per block in plain order.
     int bh, n_items, items[2];
-    if (block_order == kOrderPairs) {
+    if (VARLEN && block_order != kOrderPlain && BH / H <= kMaxRankedBatch) {
+        // Variable lengths: the longest sequences' blocks first, then the
+        // schedule's order within each sequence.
+        const int per_b = H * (block_order == kOrderPairs ? (n_qtiles + 1) / 2 : n_qtiles);
+        const int r = (int)blockIdx.x / per_b, rest = (int)blockIdx.x % per_b, k = rest / H;
+        bh = batch_of_rank(seqlens, BH / H, T, r) * H + rest % H;
+        items[0] = n_qtiles - 1 - k;
+        items[1] = k;
+        n_items = (block_order == kOrderPairs && k < items[0]) ? 2 : 1;
+    } else if (block_order == kOrderPairs) {
         int pair;
         pair_schedule((int)blockIdx.x, (BH / H) * KV, H / KV, pair, bh);
         items[0] = n_qtiles - 1 - pair;
