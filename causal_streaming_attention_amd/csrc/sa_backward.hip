@@ -567,7 +567,8 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
 //                       8 keys of one query per lane)
 // with the dS and K loads of the next four tiles in flight, since the pass
 // streams the workspace from memory.  Each lane ends with 4-float runs of
-// one query's dQ row: dQ = s * sum, stored with 16-byte writes.
+// one query's dQ row: dQ = s * sum, which goes through LDS to be stored as
+// whole rows.
 // ---------------------------------------------------------------------------
 constexpr int kDqWaves = 4;
 constexpr int kDqRows = 32 * kDqWaves;
@@ -860,13 +861,31 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
             }
             return;
         }
-        float* dq = dQ + (((size_t)b * H + h) * T + q) * kHeadDim;
+        // The wave's 32 dQ rows (8 KB, contiguous in the plane) go through
+        // LDS so that each store writes four whole rows: row r sits in this
+        // wave's own 16 rows of K buffer r / 8 (no other wave reads or fills
+        // them, and the drain above has landed this wave's last K copies),
+        // 256 bytes at (r % 8) 256, its 16-byte chunk c at c ^ (r % 16).
+        // The stores are non-temporal: nothing here reads dQ again.
+        char* stage = (char*)&lds[0][0] + 2048 * wave;
+        auto chunk_at = [&](int r, int c) {
+            return (f32x4*)(stage + (r >> 3) * (kKTileHalves * 2) + (r & 7) * 256 + ((c ^ (r & 15)) << 4));
+        };
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
             f32x4 v0 = {acc0[4 * rg], acc0[4 * rg + 1], acc0[4 * rg + 2], acc0[4 * rg + 3]};
             f32x4 v1 = {acc1[4 * rg], acc1[4 * rg + 1], acc1[4 * rg + 2], acc1[4 * rg + 3]};
-            *(f32x4*)(dq + 8 * rg + 4 * hi) = v0 * scale;
-            *(f32x4*)(dq + 32 + 8 * rg + 4 * hi) = v1 * scale;
+            *chunk_at(l32, 2 * rg + hi) = v0 * scale;
+            *chunk_at(l32, 8 + 2 * rg + hi) = v1 * scale;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float* dq = dQ + (((size_t)b * H + h) * T + (q - l32)) * kHeadDim;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = 4 * j + (lane >> 4), c = lane & 15;
+            __builtin_nontemporal_store(*chunk_at(r, c), (f32x4*)(dq + r * kHeadDim + 4 * c));
         }
     };
     process(items[0]);
