@@ -65,7 +65,8 @@ __global__ __launch_bounds__(kRowThreads) void sa_row_terms_kernel(const half_t*
 }
 
 // ---------------------------------------------------------------------------
-// Key pass.  One workgroup per (batch, K/V head, 64-key tile kt); 2 GW waves:
+// Key pass.  One workgroup per (batch, K/V head, 64-key tile kt), or per pair
+// of key tiles (p, nkt - 1 - p) taken one after the other; 2 GW waves:
 // wave (slot, khalf) takes query heads kv G + slot, + GW, ... of the group in
 // turn and owns keys kt * 64 + 32 khalf + 0..31.  Each wave walks its head's
 // 32-query sub-tiles from the last down to the diagonal one (the pages'
@@ -168,21 +169,30 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     const int slot = wave >> 1, khalf = wave & 1;
     const bool store_ds = dS != nullptr;
 
-    int kt, bkv;
+    int kt_first, kt_second = -1, bkv;
     if (VARLEN && block_order == 0 && BKV / KV <= kMaxRankedBatch) {
         // Variable lengths: the longest sequences' key tiles first (their
         // walks are the longest), key tile 0 first within each.
         const int per_b = KV * nkt;
         const int r = (int)blockIdx.x / per_b, rest = (int)blockIdx.x % per_b;
-        kt = rest / KV;
+        kt_first = rest / KV;
         bkv = batch_of_rank(seqlens, BKV / KV, T, r) * KV + rest % KV;
+    } else if (!VARLEN && block_order == kOrderKeyPairs) {
+        // Key tiles p and nkt - 1 - p: every workgroup walks the same number
+        // of sub-tiles (causal), so a grid that fits the chip at once ends
+        // together instead of leaving a second round to the dispatcher.
+        const int p = (int)(blockIdx.x / BKV);
+        bkv = (int)(blockIdx.x % BKV);
+        kt_first = p;
+        if (nkt - 1 - p != p) kt_second = nkt - 1 - p;
     } else if (block_order == 0) {  // key tile 0 first: it walks every query
-        kt = (int)(blockIdx.x / BKV);
+        kt_first = (int)(blockIdx.x / BKV);
         bkv = (int)(blockIdx.x % BKV);
     } else {
-        kt = (int)(blockIdx.x % nkt);
+        kt_first = (int)(blockIdx.x % nkt);
         bkv = (int)(blockIdx.x / nkt);
     }
+    auto process = [&](const int kt) {
     const int b = bkv / KV, kv = bkv % KV, G = H / KV;
     const int len = VARLEN ? min(max(seqlens[b], 0), T) : T;
     const int kbase = kt * kTile + 32 * khalf;  // this wave's first key
@@ -552,6 +562,14 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
         if (acc) v += *out;
         *out = v;
     }
+    };
+    process(kt_first);
+    if constexpr (!VARLEN) {
+        if (kt_second >= 0) {
+            __syncthreads();  // the first tile's group sums have been read from LDS
+            process(kt_second);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -918,6 +936,10 @@ void launch_key_gw(int GW, dim3 grid, hipStream_t stream, const half_t* Q, const
 #undef SA_KEY_LAUNCH
 }
 
+// Key-pass workgroups one CU holds at once: two waves per SIMD at 256
+// registers (8 waves per CU) and the staging buffers' LDS (34 KB per wave pair).
+int key_wgs_per_cu(int GW) { return GW >= 3 ? 1 : 4 / GW; }
+
 // Wave pairs per key-pass workgroup: the largest divisor of the group size
 // that is at most 4.
 int key_gw(int G) {
@@ -965,12 +987,19 @@ hipError_t launch_key_pass_chunk(const Shape& sh, const Chunk& ch, const void* Q
     const int nkt = chunk_key_tiles(sh, ch), BKV = sh.batch * sh.kv_heads;
     if (nkt <= 0) return hipSuccess;
     const int GW = key_gw(sh.heads / sh.kv_heads);
-    dim3 grid((unsigned)((size_t)BKV * nkt));
+    // Paired key tiles when single tiles take between one and two rounds of
+    // the chip and the walks shrink linearly (causal, every chunk row down
+    // to the diagonal): the pairs then fill it once, all of the same length.
+    const size_t singles = (size_t)BKV * nkt, slots = (size_t)kChipCUs * key_wgs_per_cu(GW);
+    const bool pairs = sh.causal && !sh.seqlens && sh.block_order == 0 && ch.q_lo == 0 && nkt >= 2 &&
+                       singles > slots && singles <= 2 * slots;
+    const int order = pairs ? kOrderKeyPairs : sh.block_order;
+    dim3 grid((unsigned)(pairs ? (size_t)BKV * ((nkt + 1) / 2) : singles));
     auto go = [&](auto causal_tag, auto varlen_tag) {
         constexpr bool C = decltype(causal_tag)::value, V = decltype(varlen_tag)::value;
         launch_key_gw<C, V>(GW, grid, stream, (const half_t*)Q, (const half_t*)K, (const half_t*)Vt,
                             (const half_t*)dO, L, D, (half_t*)dS, dK, dVt, sh.seqlens, c, s, sh.T, sh.heads,
-                            sh.kv_heads, nkt, BKV, sh.block_order, ch, sh.v_rows, kproj, vproj);
+                            sh.kv_heads, nkt, BKV, order, ch, sh.v_rows, kproj, vproj);
     };
     using T_ = std::true_type;
     using F_ = std::false_type;

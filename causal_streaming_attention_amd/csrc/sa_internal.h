@@ -23,7 +23,12 @@ struct Shape {
 // block in natural order (the caller's block_order = 1).  Every schedule
 // gives bitwise the same results.
 constexpr int kOrderPairs = 0, kOrderPlain = 1, kOrderSingle = 2;
-constexpr size_t kSingleTileGridMax = 512;
+// The key pass's own pairing: one workgroup takes key tiles p and nkt - 1 - p
+// of a (batch, K/V head) one after the other (causal walks that add up to the
+// same length), used when that grid fits the chip in one round.
+constexpr int kOrderKeyPairs = 3;
+constexpr size_t kChipCUs = 256;  // MI355X: 8 XCDs of 32 CUs
+constexpr size_t kSingleTileGridMax = 2 * kChipCUs;
 inline int tile_schedule(const Shape& sh, size_t units, int n_tiles) {
     if (sh.block_order == 1) return kOrderPlain;
     return units * (size_t)n_tiles <= kSingleTileGridMax ? kOrderSingle : kOrderPairs;

@@ -223,6 +223,22 @@ def test_block_orders_agree_bitwise_on_small_grids(B, T, H, KV, causal, seqlens)
             assert np.array_equal(a[k], b[k], equal_nan=True), f"{path}: {k} differs between block orders"
 
 
+@pytest.mark.parametrize("B,T,H,KV", [
+    (1, 2112, 32, 8),    # 33 key tiles x 8 K/V heads: 16 pairs and the middle tile alone; 4 wave pairs per group
+    (1, 2560, 32, 16),   # 40 key tiles x 16 K/V heads, 2 wave pairs per group
+])
+def test_key_tile_pairs_against_the_oracle_and_the_plain_order(B, T, H, KV):
+    """Where single key tiles need between one and two rounds of the chip, each key-pass workgroup takes key
+    tiles p and nkt - 1 - p one after the other: every output against the oracle, and bitwise the plain
+    order (one tile per workgroup)."""
+    say(f"case key tile pairs B={B} T={T} H={H} KV={KV}")
+    x = make_inputs(B, T, H, KV, seed=60 + T)
+    got = _check_all(x, True, f"key tile pairs T={T} KV={KV}")
+    _, plain = run_gpu(x, True, block_order=1)
+    for k in got:
+        assert np.array_equal(got[k], plain[k], equal_nan=True), f"{k} differs from the plain order"
+
+
 def test_grouped_heads_equal_repeated_heads():
     say("case gqa-vs-mha")
     x = make_inputs(1, 256, 8, 2, seed=21)
