@@ -3,12 +3,17 @@
 each (so one, two, three and four wave pairs per key-pass workgroup, and wave
 slots that walk several heads), causal or not, random length masks (zero and
 full lengths included), both backwards, V as rows or V^T, both block orders.
-Every output against the oracle.  Needs an MI355X."""
+Every output against the oracle; for the split backward, also the chunked
+backward with its smallest workspace (one 128-row block per chunk): D and dQ
+bitwise the split backward's, dK and dV within rounding.  Needs an
+MI355X."""
 import numpy as np
 import pytest
 
 from causal_streaming_attention_amd.workloads import make_inputs
+import causal_streaming_attention_amd as sa
 from parity_util import check_forward, check_grad, full_reference, rel_l2, run_gpu, say
+from test_gpu_chunked import _chunked
 
 pytestmark = pytest.mark.gpu
 
@@ -42,7 +47,7 @@ CASES = _cases()
 def test_sweep(name, B, T, H, KV, causal, seqlens, path, v_rows, order):
     say(f"case sweep {name}")
     x = make_inputs(B, T, H, KV, seed=3000 + B * 7 + T + H, seqlens=seqlens)
-    _, got = run_gpu(x, causal, block_order=order, path=path, v_rows=v_rows)
+    buf, got = run_gpu(x, causal, block_order=order, path=path, v_rows=v_rows)
     ref = full_reference(x, causal)
     check_forward(got["O"], got["L"], ref["O"], ref["L"], name)
     for k in ("dQ", "dK", "dVt"):
@@ -52,3 +57,9 @@ def test_sweep(name, B, T, H, KV, causal, seqlens, path, v_rows, order):
         for b, n in enumerate(seqlens):
             assert np.all(got["dQ"][b, :, n:] == 0) and np.all(got["D"][b, :, n:] == 0), name
             assert np.all(got["dK"][b, :, n:] == 0) and np.all(got["dVt"][b, :, :, n:] == 0), name
+    if path == "split":
+        ch = _chunked(buf, sa.sa_backward_chunked_min_bytes(buf.shape))
+        for k in ("D", "dQ"):
+            assert np.array_equal(ch[k], got[k]), f"{name}: chunked {k} differs from the split backward"
+        for k in ("dK", "dVt"):
+            assert rel_l2(ch[k], got[k]) <= 1e-5, f"{name}: chunked {k} differs from the split backward"
