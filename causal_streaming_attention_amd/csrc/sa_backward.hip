@@ -209,36 +209,42 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
 
     const size_t kv_off = ((size_t)b * KV + kv) * (size_t)T * kHeadDim;
 
-    // K^T as the B operand of S = Q K^T: lane (key, hi) holds K[key][16 s + 8 hi + 0..7].
-    half8 kf[4];
-    {
-        const half_t* kp = K + kv_off + (size_t)key * kHeadDim + 8 * hi;
+    // The score and dP products' B operands, held for the whole walk.  A key
+    // tile past the length (variable lengths) walks nothing and loads
+    // neither: its dK and dV are the zeros the group sum below writes.
+    // n_items is the same for every wave of the workgroup, so the barriers
+    // stay paired.
+    half8 kf[4], vf[4];
+    if (!VARLEN || n_items > 0) {
+        // K^T as the B operand of S = Q K^T: lane (key, hi) holds K[key][16 s + 8 hi + 0..7].
+        {
+            const half_t* kp = K + kv_off + (size_t)key * kHeadDim + 8 * hi;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) kf[q4] = *(const half8*)(kp + 16 * q4);
-    }
-    // V^T as the B operand of dP = dO V^T: lane (key, hi) needs V^T[16 s + 8 hi + 0..7][key],
-    // a row of V when V comes as rows, else a column of the V^T tile: stage
-    // that tile once and read it transposed.
-    half8 vf[4];
-    if (v_rows) {
-        const half_t* vp = Vt + kv_off + (size_t)key * kHeadDim + 8 * hi;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) vf[q4] = *(const half8*)(vp + 16 * q4);
-    } else {
-        half_t* vt_lds = (half_t*)smem;
-        for (int chunk = tid; chunk < 512; chunk += kThreads) {
-            int row = chunk >> 3, col = (chunk & 7) * 8;
-            *(uint4*)&vt_lds[row * kLdsRow + col] =
-                *(const uint4*)(Vt + kv_off + (size_t)row * T + kt * kTile + col);
+            for (int q4 = 0; q4 < 4; ++q4) kf[q4] = *(const half8*)(kp + 16 * q4);
         }
-        __syncthreads();
+        // V^T as the B operand of dP = dO V^T: lane (key, hi) needs V^T[16 s + 8 hi + 0..7][key],
+        // a row of V when V comes as rows, else a column of the V^T tile: stage
+        // that tile once and read it transposed.
+        if (v_rows) {
+            const half_t* vp = Vt + kv_off + (size_t)key * kHeadDim + 8 * hi;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            half4 lo = lds_read_tr(vt_lds + tr_offset(lane, 16 * q4, 16 * q4 + 8, 32 * khalf));
-            half4 hi4 = lds_read_tr(vt_lds + tr_offset(lane, 16 * q4 + 4, 16 * q4 + 12, 32 * khalf));
-            vf[q4] = cat(lo, hi4);
+            for (int q4 = 0; q4 < 4; ++q4) vf[q4] = *(const half8*)(vp + 16 * q4);
+        } else {
+            half_t* vt_lds = (half_t*)smem;
+            for (int chunk = tid; chunk < 512; chunk += kThreads) {
+                int row = chunk >> 3, col = (chunk & 7) * 8;
+                *(uint4*)&vt_lds[row * kLdsRow + col] =
+                    *(const uint4*)(Vt + kv_off + (size_t)row * T + kt * kTile + col);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                half4 lo = lds_read_tr(vt_lds + tr_offset(lane, 16 * q4, 16 * q4 + 8, 32 * khalf));
+                half4 hi4 = lds_read_tr(vt_lds + tr_offset(lane, 16 * q4 + 4, 16 * q4 + 12, 32 * khalf));
+                vf[q4] = cat(lo, hi4);
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
 
     f32x16 dkacc0 = zero16(), dkacc1 = zero16(), dvacc0 = zero16(), dvacc1 = zero16();
@@ -743,101 +749,107 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
         };
 
         f32x16 acc0 = zero16(), acc1 = zero16();
-        // dS tile kt lives in register slot kt % 5 from step kt - 4 to step kt.
-        half8 sl0[4], sl1[4], sl2[4], sl3[4], sl4[4];
-        issue(0, sl0);
-        issue(1, sl1);
-        issue(2, sl2);
-        issue(3, sl3);
-        asm volatile("s_waitcnt vmcnt(22)" ::: "memory");  // K tile 0 (and older) landed
-        __builtin_amdgcn_s_barrier();
-
-        auto step = [&](const int kt, half8 (&cur)[4], half8 (&ahead)[4]) {
-            issue(kt + kDqLead, ahead);
-            // dS tile kt, issued four steps back: 24 loads are younger.  The
-            // wait ties the slot and sits on every path, also where the tile
-            // is not used (a padding step of the unrolled loop, or a tile past
-            // this wave's rows): the compiler must not reuse or copy the
-            // slot's registers (say, for the next step's addresses) while its
-            // loads may still land in them.
-            static_assert((kDqLead) * kDqVmPerStep == 24, "the s_waitcnt immediate below");
-            asm volatile("s_waitcnt vmcnt(24)" : "+v"(cur[0]), "+v"(cur[1]), "+v"(cur[2]), "+v"(cur[3]));
-            if (kt >= kt_end) return;  // padding step: loads only
-            if (kt < kt_end_w) {
-                // The block goes through this wave's LDS copy (each 1 KB run
-                // padded by 64 bytes between its two 512-byte halves) and comes
-                // back transposed: lane (query l32, hi) gets the 8 keys of
-                // k-step s4, 16 s4 + 8 hi + 0..7, of its query.
-                half_t* dw = dsl[wave];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) lds_write16_async(dw + kDsRunHalves * u + ds_slot, cur[u]);
-                half4 g[8];
-#pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) {
-                    g[2 * s4] = lds_read_tr_async(dw + ds_tr0[s4 >> 1] + 128 * (s4 & 1));
-                    g[2 * s4 + 1] = lds_read_tr_async(dw + ds_tr0[s4 >> 1] + 128 * (s4 & 1) + 32);
-                }
-                const half_t* Ks = lds[kt % kDqDepth];
-                half4 t[16];
-#pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) {
-                    // A = K^T: lane (d, hi) holds K[16 s4 + 8 hi + 0..7][d].
-                    const int r0 = 16 * s4 + 8 * hi + trr;
-                    t[4 * s4 + 0] = lds_read_tr_async(Ks + r0 * kHeadDim + (((trc >> 3) ^ swz_key_k(r0)) << 3) + (trc & 7));
-                    t[4 * s4 + 1] = lds_read_tr_async(Ks + (r0 + 4) * kHeadDim +
-                                                      (((trc >> 3) ^ swz_key_k(r0 + 4)) << 3) + (trc & 7));
-                    t[4 * s4 + 2] = lds_read_tr_async(Ks + r0 * kHeadDim +
-                                                      ((((trc + 32) >> 3) ^ swz_key_k(r0)) << 3) + (trc & 7));
-                    t[4 * s4 + 3] = lds_read_tr_async(Ks + (r0 + 4) * kHeadDim +
-                                                      ((((trc + 32) >> 3) ^ swz_key_k(r0 + 4)) << 3) + (trc & 7));
-                }
-                lds_wait(t[0], t[1], t[2], t[3], t[4], t[5], t[6], t[7]);
-                lds_wait(t[8], t[9], t[10], t[11], t[12], t[13], t[14], t[15]);
-                lds_wait(g[0], g[1], g[2], g[3], g[4], g[5], g[6], g[7]);
-                if (VARLEN && (kt + 1) * kTile > len) {
-                    // Keys at or past the length: the DMA brought whatever
-                    // the padding holds; their dS is zero, so zero K too.
-#pragma unroll
-                    for (int s4 = 0; s4 < 4; ++s4)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int key = kt * kTile + 16 * s4 + 8 * hi + 4 * (e & 1) + 0;
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                if (key + i >= len) t[4 * s4 + e][i] = (half_t)0.0f;
-                        }
-                }
-#pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) {
-                    const half8 bs = cat(g[2 * s4], g[2 * s4 + 1]);
-                    acc0 = mfma32(cat(t[4 * s4 + 0], t[4 * s4 + 1]), bs, acc0);
-                    acc1 = mfma32(cat(t[4 * s4 + 2], t[4 * s4 + 3]), bs, acc1);
-                }
-            }
-            // K tile kt + 1 (and every older load) has landed in LDS; every
-            // wave is done reading buffer kt % 5 before it is refilled.
-            asm volatile("s_waitcnt vmcnt(22)" ::: "memory");
+        // An item whose rows are all padding (variable lengths) loads and walks
+        // nothing: its rows are written as zeros below.  kt_end is the same
+        // for every wave of the workgroup, so the barriers inside stay paired.
+        if (!VARLEN || kt_end > 0) {
+            // dS tile kt lives in register slot kt % 5 from step kt - 4 to step kt.
+            half8 sl0[4], sl1[4], sl2[4], sl3[4], sl4[4];
+            issue(0, sl0);
+            issue(1, sl1);
+            issue(2, sl2);
+            issue(3, sl3);
+            asm volatile("s_waitcnt vmcnt(22)" ::: "memory");  // K tile 0 (and older) landed
             __builtin_amdgcn_s_barrier();
-        };
-        static_assert(kDqDepth == 5, "five unrolled steps below");
-        for (int kt = 0; kt < kt_end; kt += kDqDepth) {
-            step(kt, sl0, sl4);
-            step(kt + 1, sl1, sl0);
-            step(kt + 2, sl2, sl1);
-            step(kt + 3, sl3, sl2);
-            step(kt + 4, sl4, sl3);
+
+            auto step = [&](const int kt, half8 (&cur)[4], half8 (&ahead)[4]) {
+                issue(kt + kDqLead, ahead);
+                // dS tile kt, issued four steps back: 24 loads are younger.  The
+                // wait ties the slot and sits on every path, also where the tile
+                // is not used (a padding step of the unrolled loop, or a tile past
+                // this wave's rows): the compiler must not reuse or copy the
+                // slot's registers (say, for the next step's addresses) while its
+                // loads may still land in them.
+                static_assert((kDqLead) * kDqVmPerStep == 24, "the s_waitcnt immediate below");
+                asm volatile("s_waitcnt vmcnt(24)" : "+v"(cur[0]), "+v"(cur[1]), "+v"(cur[2]), "+v"(cur[3]));
+                if (kt >= kt_end) return;  // padding step: loads only
+                if (kt < kt_end_w) {
+                    // The block goes through this wave's LDS copy (each 1 KB run
+                    // padded by 64 bytes between its two 512-byte halves) and comes
+                    // back transposed: lane (query l32, hi) gets the 8 keys of
+                    // k-step s4, 16 s4 + 8 hi + 0..7, of its query.
+                    half_t* dw = dsl[wave];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) lds_write16_async(dw + kDsRunHalves * u + ds_slot, cur[u]);
+                    half4 g[8];
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        g[2 * s4] = lds_read_tr_async(dw + ds_tr0[s4 >> 1] + 128 * (s4 & 1));
+                        g[2 * s4 + 1] = lds_read_tr_async(dw + ds_tr0[s4 >> 1] + 128 * (s4 & 1) + 32);
+                    }
+                    const half_t* Ks = lds[kt % kDqDepth];
+                    half4 t[16];
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        // A = K^T: lane (d, hi) holds K[16 s4 + 8 hi + 0..7][d].
+                        const int r0 = 16 * s4 + 8 * hi + trr;
+                        t[4 * s4 + 0] = lds_read_tr_async(Ks + r0 * kHeadDim +
+                                                          (((trc >> 3) ^ swz_key_k(r0)) << 3) + (trc & 7));
+                        t[4 * s4 + 1] = lds_read_tr_async(Ks + (r0 + 4) * kHeadDim +
+                                                          (((trc >> 3) ^ swz_key_k(r0 + 4)) << 3) + (trc & 7));
+                        t[4 * s4 + 2] = lds_read_tr_async(Ks + r0 * kHeadDim +
+                                                          ((((trc + 32) >> 3) ^ swz_key_k(r0)) << 3) + (trc & 7));
+                        t[4 * s4 + 3] = lds_read_tr_async(Ks + (r0 + 4) * kHeadDim +
+                                                          ((((trc + 32) >> 3) ^ swz_key_k(r0 + 4)) << 3) + (trc & 7));
+                    }
+                    lds_wait(t[0], t[1], t[2], t[3], t[4], t[5], t[6], t[7]);
+                    lds_wait(t[8], t[9], t[10], t[11], t[12], t[13], t[14], t[15]);
+                    lds_wait(g[0], g[1], g[2], g[3], g[4], g[5], g[6], g[7]);
+                    if (VARLEN && (kt + 1) * kTile > len) {
+                        // Keys at or past the length: the DMA brought whatever
+                        // the padding holds; their dS is zero, so zero K too.
+#pragma unroll
+                        for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const int key = kt * kTile + 16 * s4 + 8 * hi + 4 * (e & 1) + 0;
+#pragma unroll
+                                for (int i = 0; i < 4; ++i)
+                                    if (key + i >= len) t[4 * s4 + e][i] = (half_t)0.0f;
+                            }
+                    }
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        const half8 bs = cat(g[2 * s4], g[2 * s4 + 1]);
+                        acc0 = mfma32(cat(t[4 * s4 + 0], t[4 * s4 + 1]), bs, acc0);
+                        acc1 = mfma32(cat(t[4 * s4 + 2], t[4 * s4 + 3]), bs, acc1);
+                    }
+                }
+                // K tile kt + 1 (and every older load) has landed in LDS; every
+                // wave is done reading buffer kt % 5 before it is refilled.
+                asm volatile("s_waitcnt vmcnt(22)" ::: "memory");
+                __builtin_amdgcn_s_barrier();
+            };
+            static_assert(kDqDepth == 5, "five unrolled steps below");
+            for (int kt = 0; kt < kt_end; kt += kDqDepth) {
+                step(kt, sl0, sl4);
+                step(kt + 1, sl1, sl0);
+                step(kt + 2, sl2, sl1);
+                step(kt + 3, sl3, sl2);
+                step(kt + 4, sl4, sl3);
+            }
+            // The padding steps (and, with no tile to walk, the prologue) leave
+            // dS loads in flight into slots nobody reads: the compiler, which does
+            // not see them, would reuse those registers in the epilogue while a
+            // late load could still land in them.  Drain them here, tying every
+            // slot so that no register of theirs is reused before the wait.
+            asm volatile("s_waitcnt vmcnt(0)"
+                         : "+v"(sl0[0]), "+v"(sl0[1]), "+v"(sl0[2]), "+v"(sl0[3]), "+v"(sl1[0]), "+v"(sl1[1]),
+                           "+v"(sl1[2]), "+v"(sl1[3]), "+v"(sl2[0]), "+v"(sl2[1]) :: "memory");
+            asm volatile("s_waitcnt vmcnt(0)"
+                         : "+v"(sl2[2]), "+v"(sl2[3]), "+v"(sl3[0]), "+v"(sl3[1]), "+v"(sl3[2]), "+v"(sl3[3]),
+                           "+v"(sl4[0]), "+v"(sl4[1]), "+v"(sl4[2]), "+v"(sl4[3]) :: "memory");
         }
-        // The padding steps (and, with no tile to walk, the prologue) leave
-        // dS loads in flight into slots nobody reads: the compiler, which does
-        // not see them, would reuse those registers in the epilogue while a
-        // late load could still land in them.  Drain them here, tying every
-        // slot so that no register of theirs is reused before the wait.
-        asm volatile("s_waitcnt vmcnt(0)"
-                     : "+v"(sl0[0]), "+v"(sl0[1]), "+v"(sl0[2]), "+v"(sl0[3]), "+v"(sl1[0]), "+v"(sl1[1]),
-                       "+v"(sl1[2]), "+v"(sl1[3]), "+v"(sl2[0]), "+v"(sl2[1]) :: "memory");
-        asm volatile("s_waitcnt vmcnt(0)"
-                     : "+v"(sl2[2]), "+v"(sl2[3]), "+v"(sl3[0]), "+v"(sl3[1]), "+v"(sl3[2]), "+v"(sl3[3]),
-                       "+v"(sl4[0]), "+v"(sl4[1]), "+v"(sl4[2]), "+v"(sl4[3]) :: "memory");
         if (!wave_rows) return;
         const float scale = (!VARLEN || q < len) ? s : 0.0f;
         if (MODE == kDqProjection) {
