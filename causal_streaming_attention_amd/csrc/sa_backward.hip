@@ -724,9 +724,12 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
         // (qh, 1), 4 KB at 2048 qh, loaded as four coalesced 1 KB runs (lane l
         // takes 16 bytes at 8 l of each).  Loads are issued on every path (see
         // below), so their tile is clamped into the workspace: row qt_l, key
-        // tiles up to kt_last.
-        const int qt_l = min(qt_w, nt - 1);
-        const int kt_last = CAUSAL ? qt_l : nt - 1;
+        // tiles up to kt_last.  With variable lengths, a wave whose rows are
+        // all padding reads the block's first row instead, and no load goes
+        // past the item's last key tile: those tiles were never written, and
+        // reading them would only stream cold memory.
+        const int qt_l = (!VARLEN || kt_end_w > 0) ? min(qt_w, nt - 1) : qt0;
+        const int kt_last = min(CAUSAL ? qt_l : nt - 1, max(kt_end - 1, 0));
         const half_t* dSw = dS + ((size_t)b * H + h) * (size_t)ch.tph * (kTile * kTile) +
                             (size_t)(2 * qh) * 1024 + 8 * lane +
                             ((CAUSAL ? (size_t)qt_l * (qt_l + 1) / 2 : (size_t)qt_l * nt) - (size_t)ch.tile0) *
