@@ -68,9 +68,12 @@ __global__ __launch_bounds__(kRowThreads) void sa_row_terms_kernel(const half_t*
 // Key pass.  One workgroup per (batch, K/V head, 64-key tile kt), or per pair
 // of key tiles (p, nkt - 1 - p) taken one after the other; 2 GW waves:
 // wave (slot, khalf) takes query heads kv G + slot, + GW, ... of the group in
-// turn and owns keys kt * 64 + 32 khalf + 0..31.  Each wave walks its head's
-// 32-query sub-tiles from the last down to the diagonal one (the pages'
-// order) on its own: it stages each sub-tile's Q, dO, L and D into a private
+// turn and owns keys kt * 64 + 32 khalf + 0..31.  (On grids too small for the
+// chip, a group of one or two heads gets more slots than heads, GW = G R:
+// slot s takes head s % G's sub-tiles sub_hi - 1 - s / G and every R-th
+// below it, and the group sum adds the R phases like heads.)  Each wave
+// walks its head's 32-query sub-tiles from the last down to the diagonal one
+// (the pages' order) on its own: it stages each sub-tile's Q, dO, L and D into a private
 // LDS double buffer with direct global-to-LDS loads, one sub-tile ahead, so
 // the loop has no workgroup barrier and the waves sharing a SIMD drift apart
 // and overlap their matrix and vector work.  Per sub-tile and wave:
@@ -205,17 +208,21 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     const int sub_lo = CAUSAL ? max(2 * kt, 2 * ch.q_lo) : 2 * ch.q_lo;
     const bool tile_live = !VARLEN || kt * kTile < len;
     const int n_sub = tile_live ? max(0, sub_hi - sub_lo) : 0;
-    const int n_items = n_sub * (G / GW);
+    // Split walk when there are more slots than heads (GW = G R): this slot's
+    // phase and its share of the sub-tiles.
+    const bool split = GW > G;
+    const int R = split ? GW / G : 1, phase = split ? slot / G : 0;
+    const int n_items = split ? (n_sub > phase ? (n_sub - phase + R - 1) / R : 0) : n_sub * (G / GW);
 
     const size_t kv_off = ((size_t)b * KV + kv) * (size_t)T * kHeadDim;
 
     // The score and dP products' B operands, held for the whole walk.  A key
     // tile past the length (variable lengths) walks nothing and loads
     // neither: its dK and dV are the zeros the group sum below writes.
-    // n_items is the same for every wave of the workgroup, so the barriers
+    // n_sub is the same for every wave of the workgroup, so the barriers
     // stay paired.
     half8 kf[4], vf[4];
-    if (!VARLEN || n_items > 0) {
+    if (!VARLEN || n_sub > 0) {
         // K^T as the B operand of S = Q K^T: lane (key, hi) holds K[key][16 s + 8 hi + 0..7].
         {
             const half_t* kp = K + kv_off + (size_t)key * kHeadDim + 8 * hi;
@@ -304,8 +311,9 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     // The dS store's per-head base, rebuilt when the walk reaches the slot's next head.
     int ds_head_id = -1;
     half_t* ds_head = dS;
-    // Items in order: for each of the slot's heads, sub-tiles from the last down.
-    int head = kv * G + slot, sub = sub_hi - 1;
+    // Items in order: for each of the slot's heads, sub-tiles from the last
+    // down (every R-th from its phase on a split walk).
+    int head = kv * G + (split ? slot % G : slot), sub = sub_hi - 1 - phase;
     if (n_items > 0) issue_item(head, sub, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the first item has landed in LDS
     // ... and K's fragments: say so to the compiler too, which otherwise keeps
@@ -376,8 +384,8 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
         // loads, not for the stores to reach memory.
         if (store_ds) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        int next_head = head, next_sub = sub - 1;
-        if (next_sub < sub_lo) {
+        int next_head = head, next_sub = sub - R;
+        if (!split && next_sub < sub_lo) {
             next_sub = sub_hi - 1;
             next_head += GW;
         }
@@ -1001,7 +1009,12 @@ hipError_t launch_key_pass_chunk(const Shape& sh, const Chunk& ch, const void* Q
                                  hipStream_t stream) {
     const int nkt = chunk_key_tiles(sh, ch), BKV = sh.batch * sh.kv_heads;
     if (nkt <= 0) return hipSuccess;
-    const int GW = key_gw(sh.heads / sh.kv_heads);
+    const int G = sh.heads / sh.kv_heads;
+    // Grids too small for the chip (at most one workgroup per CU) with walks
+    // long enough to share (T >= 512: at least 16 sub-tiles on key tile 0): a
+    // group of one or two query heads walks its sub-tiles in 4 / G interleaved
+    // phases, one wave pair each, four wave pairs per workgroup.
+    const int GW = (G <= 2 && (size_t)BKV * nkt <= kChipCUs && sh.T >= 16 * kSubRows) ? 4 : key_gw(G);
     // Paired key tiles when single tiles take between one and two rounds of
     // the chip and the walks shrink linearly (causal, every chunk row down
     // to the diagonal): the pairs then fill it once, all of the same length.

@@ -52,6 +52,11 @@ SMALL = [
     ("single_tile_t64_varlen_full", 3, 64, 2, 2, False, [0, 17, 64]),
     ("all_empty_varlen_causal", 2, 128, 2, 1, True, [0, 0]),
     ("gqa16_t128_causal", 1, 128, 16, 1, True, None),
+    # grids too small for the chip: groups of one or two heads walk their
+    # sub-tiles in interleaved phases (4 / G wave pairs per head)
+    ("gqa2_t768_causal_split_walk", 1, 768, 2, 1, True, None),
+    ("mha_t512_b2_full_split_walk", 2, 512, 3, 3, False, None),
+    ("varlen_mha_t640_causal_split_walk", 2, 640, 2, 2, True, [640, 201]),
 ]
 
 
