@@ -419,16 +419,19 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
         // its buffer takes the next item.
         half4 t[16];
         read_transposed((const half_t*)(wstage + (it == 0 ? buf : buf ^ 1) * kItemBytes), t);
-        if (it + 1 < n_items) issue_item(next_head, next_sub, buf ^ 1);
+        // Always issued (the last item loads its own rows again into the free
+        // buffer), so that the loads share a block with the products below
+        // and go out between them.  Raised wave priority from here to the end
+        // of the item: of the two waves on a SIMD, the one past its operand
+        // reads and waits (with matrix and vector work in hand) issues first.
+        const bool more = it + 1 < n_items;
+        __builtin_amdgcn_s_setprio(1);
+        issue_item(more ? next_head : head, more ? next_sub : sub, buf ^ 1);
 
         // A block with no admitted pair (the diagonal sub-tile of the upper key
         // half, padding) goes through the same code: the mask makes its P and
         // dS exact zeros.
         f32x16 sacc = zero16(), pacc = zero16();
-        // Raised wave priority from here to the end of the item: of the two
-        // waves on a SIMD, the one past its operand reads and waits (with
-        // matrix and vector work in hand) issues first.
-        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) sacc = mfma32(qa[q4], kf[q4], sacc);
 #pragma unroll
@@ -439,6 +442,10 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
             lv[rg] = *(const f32x4*)(Ls + 8 * rg + 4 * hi);
             dv[rg] = *(const f32x4*)(Ds + 8 * rg + 4 * hi);
         }
+        // The next item's direct loads between this item's score and dP products.
+        SA_SGB(0x008, 1); SA_SGB(0x010, 2); SA_SGB(0x008, 1); SA_SGB(0x010, 2);
+        SA_SGB(0x008, 1); SA_SGB(0x010, 2); SA_SGB(0x008, 1); SA_SGB(0x010, 2);
+        SA_SGB(0x008, 1); SA_SGB(0x010, 2); SA_SGB(0x008, 3);
         // The previous item's products go into the matrix pipe behind these,
         // one between every few of this item's vector instructions.
         __builtin_amdgcn_sched_barrier(0);
