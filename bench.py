@@ -81,6 +81,30 @@ def load_traffic(kernel: str, workload: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+def device_info():
+    """The denominator's inputs as the device reports them: CU count and name from the runtime, the
+    maximum shader clock from rocminfo (a child process), or None where unavailable."""
+    import subprocess
+    import torch
+    info = {"peak_denominator": "256 CUs x 2.4 GHz x 4096 fp16 FLOP/clk/CU = %.1f TFLOP/s" % PEAK_TFLOPS}
+    try:
+        p = torch.cuda.get_device_properties(0)
+        info.update({"name": p.name, "arch": getattr(p, "gcnArchName", None), "cu_count": p.multi_processor_count})
+    except (RuntimeError, AssertionError):
+        pass
+    try:
+        r = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=30)
+        gpu = r.stdout.split("gfx950", 1)
+        if len(gpu) == 2:
+            for line in gpu[1].splitlines():
+                if "Max Clock Freq" in line:
+                    info["max_clock_mhz"] = int("".join(ch for ch in line.split(":", 1)[1] if ch.isdigit()))
+                    break
+    except (OSError, ValueError, subprocess.SubprocessError):
+        pass
+    return info
+
+
 def gpu_state():
     """Shader/memory clocks and package power from rocm-smi (a child process), or None."""
     import subprocess
@@ -714,6 +738,8 @@ def main():
         out["cold"] = cold
     if state_before is not None or state_after is not None:
         out["gpu_state"] = {"before": state_before, "after": state_after}
+    if not args.headline_only:
+        out["device"] = device_info()
     if two_pass is not None:
         out["two_pass_backward"] = two_pass
     if v_rows is not None:
