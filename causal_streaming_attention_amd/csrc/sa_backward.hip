@@ -29,38 +29,46 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // Row terms: D[b][h][i] = sum_d dO[b][h][i][d] * O[b][i][h*64 + d] in binary32
-// (each fp16 widened, fused multiply-adds), 0 on padded rows.  Eight lanes
-// per row, 16 bytes each of dO and O, reduced by three lane exchanges.
+// (each fp16 widened, fused multiply-adds), 0 on padded rows.  A block takes
+// 64 rows of one (batch, head) (T is a multiple of 64); eight lanes per row,
+// 16 bytes each of dO and O, reduced by three lane exchanges; each thread
+// takes two rows 32 apart, so that all four of its loads are in flight at once.
 // ---------------------------------------------------------------------------
 constexpr int kRowThreads = 256;
-constexpr int kRowsPerBlock = kRowThreads / 8;
+constexpr int kRowsPerBlock = 64;
 
 template <bool VARLEN>
 __global__ __launch_bounds__(kRowThreads) void sa_row_terms_kernel(const half_t* __restrict__ dO,
                                                                     const half_t* __restrict__ O,
                                                                     float* __restrict__ D,
                                                                     const int32_t* __restrict__ seqlens, int T,
-                                                                    int H, long long rows) {
-    const long long row = (long long)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 3);
-    const int part = threadIdx.x & 7;
-    float acc = 0.0f;
-    const bool in = row < rows;
-    int i = 0, b = 0, h = 0;
-    if (in) {
-        i = (int)(row % T);
-        h = (int)((row / T) % H);
-        b = (int)(row / ((long long)T * H));
-        half8 g = *(const half8*)(dO + (size_t)row * kHeadDim + 8 * part);
-        half8 o = *(const half8*)(O + (((size_t)b * T + i) * H + h) * kHeadDim + 8 * part);
+                                                                    int H) {
+    const int tiles = T / kRowsPerBlock;
+    const int bh = (int)blockIdx.x / tiles, i0 = ((int)blockIdx.x % tiles) * kRowsPerBlock;
+    const int b = bh / H, h = bh % H;
+    const int part = threadIdx.x & 7, r = threadIdx.x >> 3;  // rows i0 + r and i0 + r + 32
+    const size_t drow = (size_t)bh * T + i0 + r;
+    const size_t orow = ((size_t)b * T + i0 + r) * H + h;
+    const half8 g0 = *(const half8*)(dO + drow * kHeadDim + 8 * part);
+    const half8 g1 = *(const half8*)(dO + (drow + 32) * kHeadDim + 8 * part);
+    const half8 o0 = *(const half8*)(O + orow * kHeadDim + 8 * part);
+    const half8 o1 = *(const half8*)(O + (orow + 32 * (size_t)H) * kHeadDim + 8 * part);
+    float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) acc = __builtin_fmaf((float)g[t], (float)o[t], acc);
+    for (int t = 0; t < 8; ++t) {
+        a0 = __builtin_fmaf((float)g0[t], (float)o0[t], a0);
+        a1 = __builtin_fmaf((float)g1[t], (float)o1[t], a1);
     }
-    acc += __shfl_xor(acc, 1);
-    acc += __shfl_xor(acc, 2);
-    acc += __shfl_xor(acc, 4);
-    if (in && part == 0) {
-        const bool valid = !VARLEN || i < min(max(seqlens[b], 0), T);
-        D[row] = valid ? acc : 0.0f;
+    a0 += __shfl_xor(a0, 1);
+    a1 += __shfl_xor(a1, 1);
+    a0 += __shfl_xor(a0, 2);
+    a1 += __shfl_xor(a1, 2);
+    a0 += __shfl_xor(a0, 4);
+    a1 += __shfl_xor(a1, 4);
+    if (part == 0) {
+        const int len = VARLEN ? min(max(seqlens[b], 0), T) : T;
+        D[drow] = (!VARLEN || i0 + r < len) ? a0 : 0.0f;
+        D[drow + 32] = (!VARLEN || i0 + r + 32 < len) ? a1 : 0.0f;
     }
 }
 
@@ -981,8 +989,7 @@ int key_gw(int G) {
 }  // namespace
 
 size_t row_terms_blocks(const Shape& sh) {
-    size_t rows = (size_t)sh.batch * sh.heads * sh.T;
-    return (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+    return (size_t)sh.batch * sh.heads * (size_t)(sh.T / kRowsPerBlock);
 }
 size_t key_pass_blocks(const Shape& sh) { return (size_t)sh.batch * sh.kv_heads * (sh.T / kTile); }
 size_t dq_pass_blocks(const Shape& sh) {
@@ -992,14 +999,13 @@ size_t dq_pass_blocks(const Shape& sh) {
 }
 
 hipError_t launch_row_terms(const Shape& sh, const void* dO, const void* O, float* D, hipStream_t stream) {
-    long long rows = (long long)sh.batch * sh.heads * sh.T;
     dim3 grid((unsigned)row_terms_blocks(sh)), block(kRowThreads);
     if (sh.seqlens)
         hipLaunchKernelGGL(sa_row_terms_kernel<true>, grid, block, 0, stream, (const half_t*)dO, (const half_t*)O,
-                           D, sh.seqlens, sh.T, sh.heads, rows);
+                           D, sh.seqlens, sh.T, sh.heads);
     else
         hipLaunchKernelGGL(sa_row_terms_kernel<false>, grid, block, 0, stream, (const half_t*)dO,
-                           (const half_t*)O, D, sh.seqlens, sh.T, sh.heads, rows);
+                           (const half_t*)O, D, sh.seqlens, sh.T, sh.heads);
     return hipGetLastError();
 }
 
