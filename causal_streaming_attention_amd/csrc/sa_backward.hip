@@ -136,15 +136,9 @@ __device__ __forceinline__ int swz(int row, int col) {
     return row * kHeadDim + (((col >> 3) ^ swz_key(row)) << 3) + (col & 7);
 }
 
-// Issue-order hint for one key-pass item: the previous item's 8 dV / dK
-// products spread through this item's vector work.
+// Issue-order hint: a group of n instructions of one kind (0x008 matrix,
+// 0x010 vector memory) at this point of the schedule.
 #define SA_SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
-#define SA_KEY_SLOT SA_SGB(0x008, 1); SA_SGB(0x002, 8)
-#define SA_KEY_INTERLEAVE()                                   \
-    do {                                                      \
-        SA_KEY_SLOT; SA_KEY_SLOT; SA_KEY_SLOT; SA_KEY_SLOT;   \
-        SA_KEY_SLOT; SA_KEY_SLOT; SA_KEY_SLOT; SA_KEY_SLOT;   \
-    } while (0)
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -454,8 +448,9 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
         SA_SGB(0x008, 1); SA_SGB(0x010, 2); SA_SGB(0x008, 1); SA_SGB(0x010, 2);
         SA_SGB(0x008, 1); SA_SGB(0x010, 2); SA_SGB(0x008, 1); SA_SGB(0x010, 2);
         SA_SGB(0x008, 1); SA_SGB(0x010, 2); SA_SGB(0x008, 3);
-        // The previous item's products go into the matrix pipe behind these,
-        // one between every few of this item's vector instructions.
+        // The previous item's products go into the matrix pipe behind these;
+        // the compiler's own schedule places them among this item's vector
+        // instructions (a fixed one-product-per-eight pattern was slower).
         __builtin_amdgcn_sched_barrier(0);
         accumulate(t, wp, wd);
         float p[16], g[16];
@@ -464,7 +459,6 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
             p[r] = exp2_fast(__builtin_fmaf(sacc[r], c, -lv[r >> 2][r & 3]));
             g[r] = p[r] * (pacc[r] - dv[r >> 2][r & 3]);
         }
-        SA_KEY_INTERLEAVE();
         const bool need_mask = (CAUSAL && qb < kbase + 31) || (VARLEN && (qb + kSubRows > len || kbase + 32 > len));
         if (need_mask) {
 #pragma unroll
