@@ -751,8 +751,15 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
                             (size_t)(2 * qh) * 1024 + 8 * lane +
                             ((CAUSAL ? (size_t)qt_l * (qt_l + 1) / 2 : (size_t)qt_l * nt) - (size_t)ch.tile0) *
                                 (kTile * kTile);
+        // Loads whose data goes unused (past the item's last key tile: the
+        // lead's overrun at the end of a walk and the unrolled loop's padding
+        // steps; every load of a wave whose rows are all padding) all read one
+        // fixed block at the start of the workspace, which stays in every L2,
+        // instead of streaming a tile again from memory.
+        const half_t* dS_idle = dS + (size_t)(2 * qh) * 1024 + 8 * lane;
+        const int kt_read = kt_end_w > 0 ? kt_last : -1;
         auto load_s = [&](int kt, half8 (&dst)[4]) {
-            const half_t* t_ = dSw + (size_t)min(kt, kt_last) * (kTile * kTile);
+            const half_t* t_ = kt <= kt_read ? dSw + (size_t)kt * (kTile * kTile) : dS_idle;
             dst[0] = gload16_stream_async(t_);
             dst[1] = gload16_stream_async(t_ + 512);
             dst[2] = gload16_stream_async(t_ + 1024);
