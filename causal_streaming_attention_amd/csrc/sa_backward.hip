@@ -29,10 +29,11 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // Row terms: D[b][h][i] = sum_d dO[b][h][i][d] * O[b][i][h*64 + d] in binary32
-// (each fp16 widened, fused multiply-adds), 0 on padded rows.  A block takes
-// 64 rows of one (batch, head) (T is a multiple of 64); eight lanes per row,
-// 16 bytes each of dO and O, reduced by three lane exchanges; each thread
-// takes two rows 32 apart, so that all four of its loads are in flight at once.
+// (each fp16 widened, fused multiply-adds), 0 on padded rows (which read
+// nothing).  A block takes 64 rows of one (batch, head) (T is a multiple of
+// 64); eight lanes per row, 16 bytes each of dO and O, reduced by three lane
+// exchanges; each thread takes two rows 32 apart, so that all four of its
+// loads are in flight at once.
 // ---------------------------------------------------------------------------
 constexpr int kRowThreads = 256;
 constexpr int kRowsPerBlock = 64;
@@ -49,10 +50,18 @@ __global__ __launch_bounds__(kRowThreads) void sa_row_terms_kernel(const half_t*
     const int part = threadIdx.x & 7, r = threadIdx.x >> 3;  // rows i0 + r and i0 + r + 32
     const size_t drow = (size_t)bh * T + i0 + r;
     const size_t orow = ((size_t)b * T + i0 + r) * H + h;
-    const half8 g0 = *(const half8*)(dO + drow * kHeadDim + 8 * part);
-    const half8 g1 = *(const half8*)(dO + (drow + 32) * kHeadDim + 8 * part);
-    const half8 o0 = *(const half8*)(O + orow * kHeadDim + 8 * part);
-    const half8 o1 = *(const half8*)(O + (orow + 32 * (size_t)H) * kHeadDim + 8 * part);
+    // Rows at or past the length (padding) get D = 0 without reading dO or O.
+    const int len = VARLEN ? min(max(seqlens[b], 0), T) : T;
+    const bool in0 = !VARLEN || i0 + r < len, in1 = !VARLEN || i0 + r + 32 < len;
+    half8 g0 = {}, g1 = {}, o0 = {}, o1 = {};
+    if (in0) {
+        g0 = *(const half8*)(dO + drow * kHeadDim + 8 * part);
+        o0 = *(const half8*)(O + orow * kHeadDim + 8 * part);
+    }
+    if (in1) {
+        g1 = *(const half8*)(dO + (drow + 32) * kHeadDim + 8 * part);
+        o1 = *(const half8*)(O + (orow + 32 * (size_t)H) * kHeadDim + 8 * part);
+    }
     float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -66,9 +75,8 @@ __global__ __launch_bounds__(kRowThreads) void sa_row_terms_kernel(const half_t*
     a0 += __shfl_xor(a0, 4);
     a1 += __shfl_xor(a1, 4);
     if (part == 0) {
-        const int len = VARLEN ? min(max(seqlens[b], 0), T) : T;
-        D[drow] = (!VARLEN || i0 + r < len) ? a0 : 0.0f;
-        D[drow + 32] = (!VARLEN || i0 + r + 32 < len) ? a1 : 0.0f;
+        D[drow] = in0 ? a0 : 0.0f;
+        D[drow + 32] = in1 ? a1 : 0.0f;
     }
 }
 
