@@ -748,11 +748,11 @@ __global__ __launch_bounds__(kDqThreads, 2) void sa_dq_kernel(const half_t* __re
         // This wave's dS block of tile (qt_w, kt): the quadrants (qh, 0) and
         // (qh, 1), 4 KB at 2048 qh, loaded as four coalesced 1 KB runs (lane l
         // takes 16 bytes at 8 l of each).  Loads are issued on every path (see
-        // below), so their tile is clamped into the workspace: row qt_l, key
-        // tiles up to kt_last.  With variable lengths, a wave whose rows are
-        // all padding reads the block's first row instead, and no load goes
-        // past the item's last key tile: those tiles were never written, and
-        // reading them would only stream cold memory.
+        // below); only tiles up to kt_last of row qt_l are read, every other
+        // load goes to the fixed block below (tiles past the item's last key
+        // tile were never written).  With variable lengths, a wave whose rows
+        // are all padding takes the block's first row as qt_l, so that the
+        // address arithmetic stays in range, and reads only the fixed block.
         const int qt_l = (!VARLEN || kt_end_w > 0) ? min(qt_w, nt - 1) : qt0;
         const int kt_last = min(CAUSAL ? qt_l : nt - 1, max(kt_end - 1, 0));
         const half_t* dSw = dS + ((size_t)b * H + h) * (size_t)ch.tph * (kTile * kTile) +
