@@ -516,15 +516,19 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // every wave is done with its staging buffers
 
-    // Group sum through LDS in slot order, then coalesced stores.
+    // Group sum through LDS in slot order, then coalesced stores: dK's and
+    // dV's partials side by side (together they fill the staging space), so
+    // one barrier covers both.
     float* red = (float*)smem;
+    float* red_v = red + GW * 64 * kRedRow;
+    static_assert(2 * KeyLds<GW>::red <= KeyLds<GW>::bytes, "dK and dV partials share the LDS");
     const size_t key_row0 = ((size_t)b * KV + kv) * T + (size_t)kt * kTile;
-    auto to_lds = [&](const f32x16& a0, const f32x16& a1) {
+    auto to_lds = [&](float* dst, const f32x16& a0, const f32x16& a1) {
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
             f32x4 v0 = {a0[4 * rg], a0[4 * rg + 1], a0[4 * rg + 2], a0[4 * rg + 3]};
             f32x4 v1 = {a1[4 * rg], a1[4 * rg + 1], a1[4 * rg + 2], a1[4 * rg + 3]};
-            float* row = &red[(slot * 64 + 32 * khalf + l32) * kRedRow + 8 * rg + 4 * hi];
+            float* row = &dst[(slot * 64 + 32 * khalf + l32) * kRedRow + 8 * rg + 4 * hi];
             *(f32x4*)row = v0;
             *(f32x4*)(row + 32) = v1;
         }
@@ -544,7 +548,8 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
         *(uint2*)(pr.b16 + at) = pack_bf16x4(v[0], v[1], v[2], v[3]);
     };
     const bool proj = kproj.f32 != nullptr;
-    to_lds(dkacc0, dkacc1);
+    to_lds(red, dkacc0, dkacc1);
+    to_lds(red_v, dvacc0, dvacc1);
     __syncthreads();
     for (int idx = tid; idx < 64 * 16; idx += kThreads) {  // dK[key][d]: 16 float4s per key
         const int kk = idx >> 4, d4 = (idx & 15) * 4;
@@ -560,15 +565,12 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
             *out = v;
         }
     }
-    __syncthreads();
-    to_lds(dvacc0, dvacc1);
-    __syncthreads();
     if (v_rows || proj) {
         for (int idx = tid; idx < 64 * 16; idx += kThreads) {  // dV[key][d]: 16 float4s per key
             const int kk = idx >> 4, d4 = (idx & 15) * 4;
-            f32x4 v = *(const f32x4*)&red[kk * kRedRow + d4];
+            f32x4 v = *(const f32x4*)&red_v[kk * kRedRow + d4];
 #pragma unroll
-            for (int g = 1; g < GW; ++g) v += *(const f32x4*)&red[(g * 64 + kk) * kRedRow + d4];
+            for (int g = 1; g < GW; ++g) v += *(const f32x4*)&red_v[(g * 64 + kk) * kRedRow + d4];
             if (proj) {
                 store_proj(vproj, kk, d4, v);
             } else {
@@ -584,9 +586,9 @@ __global__ __launch_bounds__(128 * GW, 2) void sa_key_kernel(
         f32x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            float a = red[(k4 + e) * kRedRow + d];
+            float a = red_v[(k4 + e) * kRedRow + d];
 #pragma unroll
-            for (int g = 1; g < GW; ++g) a += red[(g * 64 + k4 + e) * kRedRow + d];
+            for (int g = 1; g < GW; ++g) a += red_v[(g * 64 + k4 + e) * kRedRow + d];
             v[e] = a;
         }
         f32x4* out = (f32x4*)(dVt + (((size_t)b * KV + kv) * kHeadDim + d) * T + (size_t)kt * kTile + k4);
